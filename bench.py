@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over its synthetic workloads:
+  1. bf16 causal GQA prefill, B=1, Hq=32, Hkv=8, N=16384, d=128 (fa_fwd)
+  2. paged-KV decode, 64 requests, lengths U{512..8192}, page 16,
+     Hq=32, Hkv=8, d=128 (fa_paged_decode: split kernel + merge kernel)
+  3. fp8 e4m3 prefill, B=2, H=16, N=8192, d=128, non-causal (fa_fwd)
+Inputs are seeded N(0,1) draws (seed 42) already resident in HBM when the
+timed region starts. Each launch is bracketed by HIP events on the stream
+it runs on; the step time is the wall time of K steps between two device
+synchronisations.
+
+Prints ONE JSON line. `value` is the bf16 causal prefill throughput in
+TFLOPS (algorithmic FLOPs: 4*d per visible (query, key) pair per query
+head; causal counts N(N+1)/2 pairs). The decode and fp8 legs are reported
+in their own objects (GB/s of algorithmic KV bytes, TFLOPS).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("prefill attention TFLOPS (% MFMA peak) + paged-decode HBM GB/s "
+          "(% peak)")
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+PREFILL = "bf16_causal_gqa_b1_hq32_hkv8_n16384_d128"
+FP8 = "fp8_b2_h16_n8192_d128"
+DECODE = "paged_decode_r64_hq32_hkv8_d128_p16"
+
+
+def prefill_flops(c):
+    """4*d FLOPs per visible (query, key) pair per query head."""
+    Nq, Nk = c["Nq"], c["Nk"]
+    if c["causal"]:
+        off = Nk - Nq
+        pairs = sum(max(0, min(Nk, i + off + 1)) for i in range(Nq))
+    else:
+        pairs = Nq * Nk
+    return 4.0 * c["d"] * pairs * c["Hq"] * c["B"]
+
+
+def decode_bytes(di, Hkv, d):
+    """K and V of every cached token read once per KV head (the query heads
+    of a group share them), plus q, o, LSE and the block-table entries."""
+    import torch
+    L = di.seq_lens.to(torch.int64)
+    kv = int(L.sum()) * Hkv * d * 2 * 2
+    B, Hq, _ = di.q.shape
+    pages = int(((L + di.page_size - 1) // di.page_size).sum())
+    return kv + B * Hq * d * 2 * 2 + B * Hq * 4 + pages * 4
+
+
+def _src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_attention_28_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, sources):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or
+    None when none exists or the kernel source changed since."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(p) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != _src_hash(sources):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(target_s=12.0):
+    """The fp64 oracle timed on this host on a bounded sample of the causal
+    prefill workload: the last R query rows of one head (full key range),
+    R grown until the run takes about target_s seconds."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    c = W.PREFILL_CONFIGS[PREFILL]
+    N, d = c["Nq"], c["d"]
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    v = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    import torch
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+               for x in (q, k, v))
+    scale = 1.0 / math.sqrt(d)
+    R, el = 16, 0.0
+    while True:
+        rows = np.arange(N - R, N)
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, scale, causal=True, rows=rows)
+        el = time.perf_counter() - t0
+        if el >= target_s / 4 or R >= N:
+            break
+        R = min(N, int(R * max(2.0, min(16.0, target_s / 4 / max(el, 1e-3)))))
+    # scale up once to land near the target
+    if el < target_s / 2 and R < N:
+        R = min(N, int(R * target_s / max(el, 1e-3) * 0.8))
+        rows = np.arange(N - R, N)
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, scale, causal=True, rows=rows)
+        el = time.perf_counter() - t0
+    flops = 4.0 * d * sum(int(r) + 1 for r in rows)
+    return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle, last {R} query rows x 1 head of the causal "
+                      f"N={N} d={d} prefill ({flops / 1e9:.1f} GFLOP, "
+                      f"{el:.1f} s)",
+            "seconds": el}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="prefill,decode,fp8",
+                    help="comma list of legs to run (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for "
+              f"--gpus {args.gpus}); multi-GPU sharding is not implemented",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import exact_attention_28_amd as fa
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    legs = [x for x in args.legs.split(",") if x]
+    stream = torch.cuda.current_stream(dev)
+
+    calls = {}
+    info = {}
+    if "prefill" in legs:
+        c = W.PREFILL_CONFIGS[PREFILL]
+        inp = W.prefill_config(PREFILL)
+        q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        calls["prefill"] = lambda q=q, k=k, v=v, o=o, lse=lse, c=c, inp=inp: fa.fa_fwd(
+            q, k, v, o, lse, c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"],
+            c["d"], inp.scale, True, fa.FA_DTYPE_BF16, None, stream)
+        info["prefill"] = dict(flops=prefill_flops(c), cfg=c)
+    if "decode" in legs:
+        c = W.DECODE_CONFIGS[DECODE]
+        di = W.decode_config(DECODE)
+        q = di.q.to(dev)
+        kp, vp = di.k_pool.to(dev), di.v_pool.to(dev)
+        bt, sl = di.block_table.to(dev), di.seq_lens.to(dev)
+        B, Hq, d = q.shape
+        npages, page, Hkv, _ = kp.shape
+        maxp = bt.shape[1]
+        need = fa.fa_paged_decode_workspace_size(B, Hq, Hkv, d, maxp, page, 0)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        od = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+        ld = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        calls["decode"] = lambda: fa.fa_paged_decode(
+            q, kp, vp, bt, sl, page, npages, B, Hq, Hkv, d, maxp, di.scale,
+            od, ld, ws if need else None, need, 0, stream)
+        info["decode"] = dict(bytes=decode_bytes(di, Hkv, d), cfg=c,
+                              kv_tokens=int(di.seq_lens.sum()))
+    if "fp8" in legs:
+        c = W.PREFILL_CONFIGS[FP8]
+        inp = W.prefill_config(FP8)
+        q8, k8, v8 = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+        o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+        l8 = torch.empty(q8.shape[:3], dtype=torch.float32, device=dev)
+        calls["fp8"] = lambda: fa.fa_fwd(
+            q8, k8, v8, o8, l8, c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"],
+            c["d"], inp.scale, False, fa.FA_DTYPE_FP8_E4M3, inp.descale,
+            stream)
+        info["fp8"] = dict(flops=prefill_flops(c), cfg=c)
+    torch.cuda.synchronize()
+    print(f"bench: inputs resident, legs={legs}", file=sys.stderr, flush=True)
+
+    order = [x for x in ("prefill", "decode", "fp8") if x in calls]
+    for _ in range(args.warmup):
+        for name in order:
+            calls[name]()
+    torch.cuda.synchronize()
+
+    ev = {n: [] for n in order}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name in order:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            calls[name]()
+            e1.record(stream)
+            ev[name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in order}
+    print("bench: timed region done " + ", ".join(
+        f"{n}={statistics.mean(ms[n]):.3f}ms" for n in order),
+        file=sys.stderr, flush=True)
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic (seeded N(0,1), no dataset)"}
+    workload = []
+    if "prefill" in order:
+        c = info["prefill"]["cfg"]
+        t = statistics.mean(ms["prefill"]) / 1e3
+        tf = info["prefill"]["flops"] / t / 1e12
+        out["value"] = tf
+        out["unit"] = "TFLOPS"
+        out["roofline"] = {
+            "kernel": "fwd_bf16_kernel<128, causal>",
+            "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+            "traffic": _traffic("fwd_bf16_causal_n16384",
+                                ["fa_fwd_bf16.hip", "fa_device.h"]),
+            "algorithmic_gflop_per_launch": info["prefill"]["flops"] / 1e9,
+            "launch_ms_mean": t * 1e3,
+            "launch_ms_min": min(ms["prefill"]),
+            "launch_ms_max": max(ms["prefill"])}
+        workload.append(f"bf16 causal GQA prefill B={c['B']} Hq={c['Hq']} "
+                        f"Hkv={c['Hkv']} N={c['Nq']} d={c['d']}")
+    if "decode" in order:
+        c = info["decode"]["cfg"]
+        t = statistics.mean(ms["decode"]) / 1e3
+        gbs = info["decode"]["bytes"] / t / 1e9
+        out["decode"] = {
+            "value": gbs, "unit": "GB/s", "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+            "roofline": {"kernel": "decode_split_kernel + decode_merge_kernel",
+                         "bound": "hbm", "achieved": gbs,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": _traffic("decode_r64",
+                                             ["fa_decode.hip", "fa_device.h"])},
+            "algorithmic_bytes": info["decode"]["bytes"],
+            "kv_tokens": info["decode"]["kv_tokens"],
+            "launch_ms_mean": t * 1e3,
+            "launch_ms_min": min(ms["decode"])}
+        workload.append(f"paged decode {c['n_req']} requests L~U{{{c['len_min']}.."
+                        f"{c['len_max']}}} page {c['page_size']} Hq={c['Hq']} "
+                        f"Hkv={c['Hkv']} d={c['d']}")
+        if "value" not in out:
+            out["value"], out["unit"] = gbs, "GB/s"
+    if "fp8" in order:
+        c = info["fp8"]["cfg"]
+        t = statistics.mean(ms["fp8"]) / 1e3
+        tf = info["fp8"]["flops"] / t / 1e12
+        out["fp8_prefill"] = {
+            "value": tf, "unit": "TFLOPS", "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
+            "launch_ms_mean": t * 1e3}
+        workload.append(f"fp8 e4m3 prefill B={c['B']} H={c['Hq']} N={c['Nq']} "
+                        f"d={c['d']}")
+        if "value" not in out:
+            out["value"], out["unit"] = tf, "TFLOPS"
+    out["config"] = {"workload": " + ".join(workload), "seed": 42,
+                     "parallelism": "single GPU"}
+    if not args.no_cpu_baseline and "prefill" in order:
+        print("bench: timing the CPU oracle baseline", file=sys.stderr,
+              flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,20 @@
+"""MI355X (gfx950) exact attention: fused prefill forward and paged decode.
+
+The computation lives in ``libfa.so`` (hand-written HIP kernels behind the
+C ABI of ``include/fa.h``); this package only binds it. Build it in-tree
+with ``python -m exact_attention_28_amd.build``.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    FA_DTYPE_BF16,
+    FA_DTYPE_F32,
+    FA_DTYPE_FP8_E4M3,
+    FaError,
+    LIB_PATH,
+    fa_fwd,
+    fa_paged_decode,
+    fa_paged_decode_workspace_size,
+    fa_strerror,
+    load_library,
+)
+from .api import attention, paged_decode  # noqa: F401

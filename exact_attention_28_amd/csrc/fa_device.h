@@ -1,0 +1,167 @@
+// fa_device.h - device-side building blocks shared by the gfx950 kernels:
+// vector types, MFMA wrappers, wave64 cross-lane helpers and the online
+// softmax update on an MFMA score tile.
+//
+// Layout convention used by every prefill kernel (the "transposed" form):
+// a wave computes S^T = K . Q^T with v_mfma_f32_32x32x*, so that in the
+// 32x32 accumulator lane l holds the scores of query row (l % 32) against
+// 16 of the 32 keys: key = 8*(v/4) + 4*(l/32) + (v%4) for accumulator
+// element v. Row statistics (max, sum) are then almost entirely lane-local
+// (the other 16 keys of the row sit in lane l ^ 32), and the same
+// accumulator feeds the B operand of O^T += V^T . P^T without leaving
+// registers. O^T keeps the row in the lane as well, so the per-row rescale
+// of the online softmax is a per-lane multiply.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+// Lazy rescale threshold in log2 units: the running maximum used as the
+// exponent reference is only raised when a new score exceeds it by more
+// than this, so exp2 arguments stay <= kTau (P <= 256, fine in fp32, bf16
+// and e4m3) while O and l are rescaled only rarely. Exact: O and l always
+// share the same reference.
+constexpr float kTau = 8.0f;
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+__device__ __forceinline__ float fast_log2(float x) {
+  return __builtin_amdgcn_logf(x);
+}
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b,
+                                                     f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b,
+                                                    f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b,
+                                                   f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+// e4m3 x e4m3 (format code 0 for both operands), no block scaling.
+__device__ __forceinline__ f32x16 mfma_32x32x64_e4m3(i32x8 a, i32x8 b,
+                                                     f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0,
+                                                         0, 0);
+}
+
+// ------------------------------------------------------- cross-lane ops
+__device__ __forceinline__ float xor_lane(float x, int mask) {
+  return __shfl_xor(x, mask, 64);
+}
+
+// ---------------------------------------------------------- conversions
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};     // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+// Four fp32 -> four OCP e4m3 bytes, byte i = x_i (round to nearest even).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float x0, float x1, float x2,
+                                                float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return (uint32_t)w;
+}
+
+// ------------------------------------------------ workgroup -> tile map
+// One workgroup computes one BM-row query tile of one (batch, query head).
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2), so the block id is remapped to give every XCD a contiguous range of
+// logical tiles; logical order is (batch, kv head) group-major, so the
+// query heads that share a KV head, and all their query tiles, run on one
+// XCD and hit the same K/V lines in its L2. Within a group, causal tiles go
+// heaviest (longest key range) first.
+struct TileIdx {
+  int b, hq, qt;
+};
+__device__ __forceinline__ TileIdx map_tile(int bid, int n_qt, int Hq,
+                                            int Hkv, int B, bool causal) {
+  const int total = n_qt * Hq * B;
+  int lid = bid;
+  if ((total & 7) == 0) lid = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int G = Hq / Hkv;
+  const int per_group = n_qt * G;
+  const int grp = lid / per_group;
+  const int rem = lid - grp * per_group;
+  const int rank = rem / G;
+  TileIdx t;
+  t.b = grp / Hkv;
+  t.hq = (grp - t.b * Hkv) * G + (rem - rank * G);
+  t.qt = causal ? (n_qt - 1 - rank) : rank;
+  return t;
+}
+
+// ---------------------------------------------- online softmax on S^T
+// State of one query row (one lane, mirrored in lane ^ 32).
+struct RowState {
+  float m;  // exponent reference in log2 units (-inf until a key is seen)
+  float l;  // this lane's partial sum of P (its 16 of every 32 keys)
+};
+
+// Applies one key tile to the running state ([Capstone §2.2 steps 3-4]
+// with the deferred normalisation of §4.2): s[] holds the raw scores of
+// NKB 32-key blocks in the transposed accumulator layout (masked entries
+// already -inf); c = scale * log2(e). On return s[] holds P = exp2(s*c -
+// m_ref) and o[] (NMB blocks of O^T) and st.l are rescaled if the
+// reference moved.
+template <int NKB, int NMB>
+__device__ __forceinline__ void online_softmax_tile(f32x16 (&s)[NKB],
+                                                    f32x16 (&o)[NMB],
+                                                    RowState& st, float c) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+  mx = fmaxf(mx, xor_lane(mx, 32));
+  const float mxs = mx * c;  // c > 0, so max commutes with the scaling
+  const bool need = mxs > st.m + kTau;
+  if (__any(need)) {
+    const float mnew = fmaxf(st.m, mxs);
+    const float alpha = (st.m == kNegInf) ? 0.f : fast_exp2(st.m - mnew);
+    st.l *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[mb][v] *= alpha;
+    st.m = mnew;
+  }
+  const float mref = (st.m == kNegInf) ? 0.f : st.m;
+  float sum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = fast_exp2(__builtin_fmaf(s[kb][v], c, -mref));
+      s[kb][v] = p;
+      sum += p;
+    }
+  st.l += sum;
+}
+
+}  // namespace fa

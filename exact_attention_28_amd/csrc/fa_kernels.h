@@ -1,0 +1,55 @@
+// fa_kernels.h - host-side launchers of the gfx950 kernels (internal).
+// Arguments have been validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  bool causal;
+  float s_q, s_k, s_v;  // fp8 per-tensor scales (1 for other dtypes)
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_fp8(const FwdArgs& a);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int num_pages, B, Hq, Hkv, d, max_pages;
+  float scale;
+  void* o;
+  float* lse;  // may be null
+  float* ws;   // split partials (null when there is a single split)
+  int pages_per_split, num_splits;
+  hipStream_t stream;
+};
+
+// Split plan shared by the workspace-size query and the launch.
+struct DecodePlan {
+  int pages_per_split;
+  int num_splits;
+  size_t workspace_bytes;
+};
+// Returns false when the requested split count cannot be honoured.
+bool plan_decode(int B, int Hq, int Hkv, int d, int max_pages,
+                 int num_splits, DecodePlan* plan);
+
+hipError_t launch_paged_decode(const DecodeArgs& a);
+
+}  // namespace fa

@@ -1,0 +1,175 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
+ *
+ * Two operations, both exact attention O = softmax(scale * Q K^T) V computed
+ * in one streaming pass with an online softmax, so the score matrix S and
+ * the probability matrix P never reach device memory:
+ *
+ *   fa_fwd           prefill / training forward over contiguous Q, K, V.
+ *   fa_paged_decode  one query token per request against a paged KV cache,
+ *                    split over workgroups and merged by log-sum-exp.
+ *
+ * Sources (cited by page and section):
+ *   [FA3-guide]  "Flash Attention 3 指南：GPU IO 优化的终极武器"
+ *                (guijiagi.com): the fp8 forward listing.
+ *   [FA3-paged]  "FlashAttention V3 实战：Hopper 架构下的 Paged KV Cache
+ *                协同优化" (ybb.press): §一 (the attention definition),
+ *                §3.1 (online softmax with tiling), §3.2 (paged KV cache).
+ *   [Capstone]   "项目三：榨干片上 SRAM——CUDA Softmax 与 Attention 算子
+ *                极致性能调优" (lilinji.mintlify.site): §1.1 (definition),
+ *                §2.2 (online softmax and the two-block merge), §4.1-4.2
+ *                (Q-outer loop order, deferred normalisation), §7.3 Q2
+ *                (causal tile skipping), appendix A Q1 (merge proof).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is DEVICE memory on the current HIP device,
+ *   allocated and owned by the caller, contiguous in the layout stated,
+ *   16-byte aligned (4-byte for fp32 LSE and the int32 tables).
+ *   The library never allocates, frees or keeps a pointer, and keeps no
+ *   state between calls: calls from several host threads are safe.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *   stream) and runs asynchronously: outputs are valid once the stream has
+ *   reached the call. Nothing inside synchronises with the host.
+ * - Inputs are read-only. Outputs are fully overwritten.
+ * - Return value: FA_OK (0) on success. A negative FA_E* code means the
+ *   arguments were rejected before anything was launched and nothing was
+ *   written. A positive value is a hipError_t reported by the launch.
+ *   No C++ exception or abort crosses this boundary.
+ * - LSE is the natural-log log-sum-exp of the scaled scores of a row,
+ *   LSE = m + ln(l) with m the row maximum and l = sum exp(s - m): the pair
+ *   (m, l) the pages keep per row ([Capstone §6.1], the row about not
+ *   writing P), folded into one fp32 number. A row that sees no key gets
+ *   O = 0 and LSE = -inf.
+ * - Head dimension d is 64 or 128.
+ */
+#ifndef EXACT_ATTENTION_FA_H
+#define EXACT_ATTENTION_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of Q, K, V (fa_fwd `dtype`). */
+#define FA_DTYPE_F32 0      /* fp32 in, fp32 O                              */
+#define FA_DTYPE_BF16 1     /* bf16 in, bf16 O (fp32 accumulation)          */
+#define FA_DTYPE_FP8_E4M3 2 /* OCP float8 e4m3fn in + per-tensor fp32
+                               scales, bf16 O                               */
+
+/* Return codes. */
+#define FA_OK 0
+#define FA_EINVAL_NULL (-1)     /* a required pointer is NULL               */
+#define FA_EINVAL_DIM (-2)      /* a size is <= 0, or a product overflows   */
+#define FA_EUNSUPPORTED_D (-3)  /* head dimension not 64 or 128             */
+#define FA_EGQA (-4)            /* Hq not a multiple of Hkv, or group too big*/
+#define FA_EDTYPE (-5)          /* unknown dtype                            */
+#define FA_EDESCALE (-6)        /* fp8 without descales, or descales given
+                                   for another dtype, or a descale <= 0     */
+#define FA_ESCALE (-7)          /* softmax scale not finite or not > 0      */
+#define FA_EPAGE (-8)           /* unsupported page size / page count       */
+#define FA_EWORKSPACE (-9)      /* workspace missing or too small           */
+#define FA_ESPLITS (-10)        /* num_splits < 0, or > 256 pages per split */
+#define FA_EALIGN (-11)         /* a tensor pointer is not 16-byte aligned
+                                   (4-byte for lse, block_table, seq_lens) */
+
+/*
+ * fa_fwd - exact attention forward, prefill / training shape.
+ *
+ * Computes, for every batch b, query head h and query row i,
+ *   S_ij = scale * <Q[b,h,i,:], K[b,h/(Hq/Hkv),j,:]>     ([Capstone §1.1])
+ *   O[b,h,i,:] = sum_j softmax_j(S_i.) V[b,h/(Hq/Hkv),j,:]
+ *   LSE[b,h,i] = ln sum_j exp(S_ij)
+ * in a single pass over K/V tiles with the online-softmax recurrence of
+ * [Capstone §2.2] in the Q-outer order with deferred 1/l of [Capstone
+ * §4.1-4.2]. S and P stay on chip.
+ *
+ * q      [B, Hq,  Nq, d]  element type `dtype`
+ * k, v   [B, Hkv, Nk, d]  element type `dtype`
+ * o      [B, Hq,  Nq, d]  fp32 for FA_DTYPE_F32, bf16 otherwise
+ * lse    [B, Hq,  Nq]     fp32; may be NULL when LSE is not wanted
+ * Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv) (grouped-query
+ *   attention; Hq == Hkv is plain multi-head attention).
+ * scale  finite and > 0 (the pages use 1/sqrt(d)).
+ * causal non-zero: key j is visible to query i iff j <= i + (Nk - Nq)
+ *   (bottom-right aligned; the lower triangle when Nq == Nk, [Capstone
+ *   §7.3 Q2]). KV tiles wholly above the diagonal are skipped. Rows that
+ *   see no key (only possible when Nq > Nk) get O = 0, LSE = -inf.
+ * qkv_descale  HOST pointer to three floats (s_q, s_k, s_v), each > 0:
+ *   the real inputs are code * s ([FA3-guide] fp8 listing, with a
+ *   per-tensor scale). Required for FA_DTYPE_FP8_E4M3, must be NULL for the
+ *   other dtypes. Read during the call only.
+ *   In the fp8 path, P is rounded to e4m3 (unscaled) before the P.V
+ *   product, as in the [FA3-guide] fp8 listing; l is summed in fp32.
+ * stream hipStream_t or NULL.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+           int causal, int dtype, const float* qkv_descale, void* stream);
+
+/*
+ * fa_paged_decode_workspace_size - bytes of device workspace that
+ * fa_paged_decode needs for these arguments (0 when it needs none).
+ * num_splits: 0 = let the library choose (the same choice fa_paged_decode
+ * makes for the same arguments), else the number of KV splits per
+ * request. Returns 0 for arguments fa_paged_decode would reject.
+ */
+size_t fa_paged_decode_workspace_size(int B, int Hq, int Hkv, int d,
+                                      int max_pages_per_seq, int page_size,
+                                      int num_splits);
+
+/*
+ * fa_paged_decode - one query token per request against a paged KV cache
+ * ([FA3-paged §3.2]: each request's cache lives in fixed-size pages that a
+ * per-request table maps to physical slots, like virtual memory).
+ *
+ * For request b with L = seq_lens[b] cached tokens, logical page p holds
+ * tokens p*page_size .. p*page_size+page_size-1 in physical page
+ * block_table[b, p]. The query attends to all L tokens (no mask inside the
+ * context; slots of the last page at or past L are ignored). Each request's
+ * pages are split into chunks processed by separate workgroups; every
+ * chunk yields a normalised partial output and its LSE, merged with the
+ * log-sum-exp form of the two-block merge identity ([Capstone §2.2 step 4],
+ * appendix A Q1).
+ *
+ * q            [B, Hq, d] bf16 (one token per request)
+ * k_pool,
+ * v_pool       [num_pages, page_size, Hkv, d] bf16 (token-major pages)
+ * block_table  [B, max_pages_per_seq] int32, row-major, device memory.
+ *              Entries past ceil(L/page_size) are never read.
+ * seq_lens     [B] int32, device memory. Values are clamped to
+ *              [0, max_pages_per_seq*page_size]. L = 0 gives O = 0 and
+ *              LSE = -inf for that request.
+ *              A referenced page id outside [0, num_pages) is never
+ *              dereferenced: that request's O and LSE become NaN.
+ * page_size    16.
+ * num_pages    number of pages in each pool (for the bounds check above).
+ * Hq % Hkv == 0 and Hq / Hkv <= 16.
+ * scale        finite and > 0.
+ * o            [B, Hq, d] bf16; lse [B, Hq] fp32 or NULL.
+ * workspace    device memory of at least
+ *              fa_paged_decode_workspace_size(B, Hq, Hkv, d,
+ *              max_pages_per_seq, page_size, num_splits) bytes, 256-byte
+ *              aligned; may be NULL when that size is 0. Its contents on
+ *              entry do not matter. Two calls that run concurrently must
+ *              not share a workspace.
+ * num_splits   0 = auto, else the number of chunks per request.
+ * stream       hipStream_t or NULL.
+ */
+int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int page_size, int num_pages, int B, int Hq, int Hkv,
+                    int d, int max_pages_per_seq, float scale, void* o,
+                    float* lse, void* workspace, size_t workspace_bytes,
+                    int num_splits, void* stream);
+
+/* fa_strerror - static, NUL-terminated description of a return code. */
+const char* fa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_FA_H */

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle
+on the same seeded inputs.
+
+Bars (max-abs error against the oracle):
+  fp32        O and LSE <= 1e-5
+  bf16        O <= 1e-2, LSE <= 1e-3
+  fp8 e4m3    O <= 6e-2 (oracle fed the same e4m3 values); LSE <= 5e-2
+              (reported bound: the pages set none for fp8 LSE)
+Rows that see no key must give O == 0 exactly and LSE == -inf.
+Reduced sizes span several tiles and ragged tails; the full workloads are
+checked on sampled rows (each output row depends only on its own query, so
+the oracle evaluates exactly those rows).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (1e-2, 1e-3), "fp8": (6e-2, 5e-2),
+       # fp32 with scores of magnitude ~300: rounding of S alone is
+       # ~1e-7 * |S| * sqrt(d) ~ 3e-4 before the softmax amplifies nothing
+       "f32_wide": (3e-4, 3e-4)}
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_28_amd as m
+    m.load_library()
+    return m
+
+
+def _gpu_fwd(fa, inp):
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    o, lse = fa.attention(q, k, v, causal=inp.causal, scale=inp.scale,
+                          descale=inp.descale)
+    torch.cuda.synchronize()
+    return o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
+
+
+def _oracle_fwd(inp, rows=None):
+    if inp.dtype == "fp8":
+        return oracle.attention_fp8(W.as_f64(inp.q), W.as_f64(inp.k),
+                                    W.as_f64(inp.v), *inp.descale, inp.scale,
+                                    causal=inp.causal, rows=rows)
+    return oracle.attention(W.as_f64(inp.q), W.as_f64(inp.k), W.as_f64(inp.v),
+                            inp.scale, causal=inp.causal, rows=rows)
+
+
+def _compare(o, lse, ro, rl, dtype, what=""):
+    to, tl = TOL[dtype]
+    assert not np.any(np.isnan(o)), what
+    dead = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), dead), what
+    assert np.all(o[dead] == 0.0), what
+    eo = float(np.max(np.abs(o - ro)))
+    el = float(np.max(np.abs(lse[~dead] - rl[~dead]), initial=0.0))
+    print(f"{what}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= to, f"{what}: O error {eo}"
+    assert el <= tl, f"{what}: LSE error {el}"
+
+
+# ---------------------------------------------------------------- sweeps
+SHAPES = [
+    # B, Hq, Hkv, Nq, Nk
+    (1, 1, 1, 1, 1),
+    (1, 2, 1, 2, 3),
+    (1, 1, 1, 17, 17),
+    (2, 4, 4, 63, 65),
+    (1, 4, 1, 64, 64),
+    (1, 8, 1, 65, 129),
+    (1, 8, 8, 127, 127),
+    (2, 8, 2, 129, 64),
+    (1, 4, 4, 1000, 1000),
+    (1, 2, 2, 300, 1000),
+    (1, 2, 1, 1000, 300),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_fwd_sweep(fa, dtype, d, causal, shape):
+    B, Hq, Hkv, Nq, Nk = shape
+    inp = W.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype=dtype, causal=causal,
+                           seed=hash((shape, d)) % 1000)
+    o, lse = _gpu_fwd(fa, inp)
+    ro, rl = _oracle_fwd(inp)
+    _compare(o, lse, ro, rl, dtype, f"{dtype} d{d} causal={causal} {shape}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_fwd_rising_scores_rescale_path(fa, dtype):
+    """Keys whose scores grow along the sequence move the running maximum
+    by more than the lazy-rescale threshold on many tiles."""
+    B, H, N, d = 1, 2, 700, 128
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    k = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    v = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    k += (np.arange(N, dtype=np.float32)[:, None] / 40.0) * np.sign(q[:, :, :1, :])
+    inp = W.PrefillInputs(*[W._to_storage(x, dtype)[0] for x in (q, k, v)],
+                          scale=1.0 / math.sqrt(d), causal=False, dtype=dtype,
+                          descale=None)
+    if dtype == "fp8":
+        inp.descale = tuple(W._to_storage(x, "fp8")[1] for x in (q, k, v))
+    o, lse = _gpu_fwd(fa, inp)
+    ro, rl = _oracle_fwd(inp)
+    assert np.max(rl) - np.min(rl) > 20          # the scores really spread
+    _compare(o, lse, ro, rl, "f32_wide" if dtype == "f32" else dtype,
+             f"rising {dtype}")
+
+
+def test_fwd_fully_masked_rows(fa):
+    inp = W.prefill_inputs(1, 2, 1, 200, 70, 128, dtype="bf16", causal=True)
+    o, lse = _gpu_fwd(fa, inp)
+    assert np.all(np.isneginf(lse[:, :, :130]))
+    assert np.all(o[:, :, :130] == 0.0)
+    ro, rl = _oracle_fwd(inp)
+    _compare(o, lse, ro, rl, "bf16", "Nq > Nk causal")
+
+
+def test_fwd_deterministic(fa):
+    inp = W.prefill_inputs(1, 4, 2, 333, 333, 128, dtype="bf16", causal=True)
+    o1, l1 = _gpu_fwd(fa, inp)
+    o2, l2 = _gpu_fwd(fa, inp)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_fwd_lse_optional(fa):
+    inp = W.prefill_inputs(1, 2, 2, 100, 100, 64, dtype="bf16")
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    o, lse = fa.attention(q, k, v, scale=inp.scale, want_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    ro, _ = _oracle_fwd(inp)
+    assert np.max(np.abs(o.double().cpu().numpy() - ro)) <= 1e-2
+
+
+# ------------------------------------------------------ full workloads
+def _sample_rows(N, rng, extra=48):
+    fixed = [0, 1, 2, 63, 64, 127, 128, 129, N // 2, N - 129, N - 128, N - 2,
+             N - 1]
+    rows = set(r for r in fixed if 0 <= r < N)
+    rows.update(rng.choice(N, size=min(extra, N), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", sorted(W.PREFILL_CONFIGS))
+def test_fwd_full_workload(fa, name):
+    c = W.PREFILL_CONFIGS[name]
+    inp = W.prefill_config(name)
+    o, lse = _gpu_fwd(fa, inp)
+    if c["Nq"] * c["Nk"] * c["B"] * c["Hq"] <= (1 << 26):
+        ro, rl = _oracle_fwd(inp)
+        _compare(o, lse, ro, rl, c["dtype"], name)
+        return
+    rng = np.random.default_rng(0)
+    rows = _sample_rows(c["Nq"], rng)
+    # (batch, head) pairs: first and last head, a middle one, and the last
+    # head of the first GQA group
+    G = c["Hq"] // c["Hkv"]
+    pairs = sorted({(0, 0), (0, c["Hq"] - 1), (c["B"] - 1, c["Hq"] // 2),
+                    (c["B"] - 1, G - 1)})
+    for b, h in pairs:
+        sub = W.PrefillInputs(inp.q[b:b + 1, h:h + 1], inp.k[b:b + 1, h // G:h // G + 1],
+                              inp.v[b:b + 1, h // G:h // G + 1], inp.scale,
+                              inp.causal, inp.dtype, inp.descale)
+        ro, rl = _oracle_fwd(sub, rows=rows)
+        _compare(o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows], ro, rl,
+                 c["dtype"], f"{name} b{b} h{h}")
+    # properties over every row: no NaN, causal row 0 of every head is V[0]
+    assert not np.any(np.isnan(o)) and np.all(np.isfinite(lse))
+    if inp.causal:
+        v0 = W.as_f64(inp.v[:, :, 0])                       # [B, Hkv, d]
+        want = np.repeat(v0, G, axis=1)
+        assert np.max(np.abs(o[:, :, 0] - want)) <= 4e-3
+
+
+# ---------------------------------------------------------------- decode
+def _gpu_decode(fa, di, num_splits=0, num_pages=None):
+    dev = torch.device("cuda:0")
+    q = di.q.to(dev)
+    kp, vp = di.k_pool.to(dev), di.v_pool.to(dev)
+    bt, sl = di.block_table.to(dev), di.seq_lens.to(dev)
+    B, Hq, d = q.shape
+    npg, page, Hkv, _ = kp.shape
+    maxp = bt.shape[1]
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = fa.fa_paged_decode_workspace_size(B, Hq, Hkv, d, maxp, page,
+                                             num_splits)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    fa.fa_paged_decode(q, kp, vp, bt, sl, page,
+                       npg if num_pages is None else num_pages, B, Hq, Hkv, d,
+                       maxp, di.scale, out, lse, ws if need else None, need,
+                       num_splits)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def _oracle_decode(di):
+    return oracle.paged_decode(W.as_f64(di.q), W.as_f64(di.k_pool),
+                               W.as_f64(di.v_pool), di.block_table.numpy(),
+                               di.seq_lens.numpy(), di.page_size, di.scale)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (32, 8), (16, 1), (6, 2)])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_decode_sweep(fa, d, hq, hkv, num_splits):
+    lens = [0, 1, 15, 16, 17, 31, 33, 100, 255, 256, 257, 1000]
+    di = W.decode_inputs(len(lens), hq, hkv, d, lens=lens, max_pages=80,
+                         seed=d + hq, extra_pages=5)
+    o, lse = _gpu_decode(fa, di, num_splits)
+    ro, rl = _oracle_decode(di)
+    _compare(o, lse, ro, rl, "bf16", f"decode d{d} {hq}/{hkv} splits={num_splits}")
+
+
+def test_decode_many_splits_and_long(fa):
+    lens = [8192, 4097, 1, 5000, 512, 8191]
+    di = W.decode_inputs(len(lens), 32, 8, 128, lens=lens, max_pages=512,
+                         seed=3)
+    for ns in (0, 2, 7, 64, 512):
+        o, lse = _gpu_decode(fa, di, ns)
+        ro, rl = _oracle_decode(di)
+        _compare(o, lse, ro, rl, "bf16", f"long decode splits={ns}")
+
+
+def test_decode_bad_page_id_gives_nan(fa):
+    di = W.decode_inputs(3, 8, 2, 128, lens=[40, 40, 40], max_pages=4, seed=1)
+    bt = di.block_table.clone()
+    bt[1, 2] = 10_000                  # past the pool
+    di.block_table = bt
+    for ns in (0, 1):
+        o, lse = _gpu_decode(fa, di, ns)
+        assert np.all(np.isnan(o[1])) and np.all(np.isnan(lse[1]))
+        assert not np.any(np.isnan(o[[0, 2]]))
+
+
+def test_decode_full_workload(fa):
+    name = next(iter(W.DECODE_CONFIGS))
+    di = W.decode_config(name)
+    o, lse = _gpu_decode(fa, di)
+    ro, rl = _oracle_decode(di)
+    _compare(o, lse, ro, rl, "bf16", name)
