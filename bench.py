@@ -87,10 +87,12 @@ def _traffic(kernel_key, sources):
 
 def cpu_baseline(target_s=12.0):
     """The fp64 oracle timed on this host on a bounded sample of the causal
-    prefill workload: the last R query rows of one head (full key range),
-    R grown until the run takes about target_s seconds."""
+    prefill workload: whole query heads (every row, every visible key)
+    sharing one KV head, as many as take about target_s seconds (the last R
+    rows of one head if even one head is slower than that)."""
     import numpy as np
     import oracle
+    import torch
     import workloads as W
     try:
         from threadpoolctl import threadpool_info
@@ -100,36 +102,36 @@ def cpu_baseline(target_s=12.0):
         threads = os.cpu_count() or 1
     c = W.PREFILL_CONFIGS[PREFILL]
     N, d = c["Nq"], c["d"]
-    rng = np.random.default_rng(42)
-    q = rng.standard_normal((1, 1, N, d)).astype(np.float32)
-    k = rng.standard_normal((1, 1, N, d)).astype(np.float32)
-    v = rng.standard_normal((1, 1, N, d)).astype(np.float32)
-    import torch
-    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
-               for x in (q, k, v))
     scale = 1.0 / math.sqrt(d)
-    R, el = 16, 0.0
-    while True:
-        rows = np.arange(N - R, N)
+
+    def draw(h):
+        rng = np.random.default_rng(42)
+        x = rng.standard_normal((1, h, N, d)).astype(np.float32)
+        return torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+
+    q1, k, v = draw(1), draw(1), draw(1)
+    t0 = time.perf_counter()
+    oracle.attention(q1, k, v, scale, causal=True)
+    el = time.perf_counter() - t0
+    heads, rows = 1, N
+    if el > target_s:
+        rows = max(1, int(N * target_s / el))
         t0 = time.perf_counter()
-        oracle.attention(q, k, v, scale, causal=True, rows=rows)
+        oracle.attention(q1, k, v, scale, causal=True,
+                         rows=np.arange(N - rows, N))
         el = time.perf_counter() - t0
-        if el >= target_s / 4 or R >= N:
-            break
-        R = min(N, int(R * max(2.0, min(16.0, target_s / 4 / max(el, 1e-3)))))
-    # scale up once to land near the target
-    if el < target_s / 2 and R < N:
-        R = min(N, int(R * target_s / max(el, 1e-3) * 0.8))
-        rows = np.arange(N - R, N)
+    elif el < target_s / 2:
+        heads = max(1, min(c["Hq"], int(round(target_s / max(el, 1e-3)))))
+        qh = draw(heads)
         t0 = time.perf_counter()
-        oracle.attention(q, k, v, scale, causal=True, rows=rows)
+        oracle.attention(qh, k, v, scale, causal=True)
         el = time.perf_counter() - t0
-    flops = 4.0 * d * sum(int(r) + 1 for r in rows)
+    flops = 4.0 * d * heads * sum(i + 1 for i in range(N - rows, N))
     return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": threads,
             "kind": "oracle",
-            "sample": f"fp64 oracle, last {R} query rows x 1 head of the causal "
-                      f"N={N} d={d} prefill ({flops / 1e9:.1f} GFLOP, "
-                      f"{el:.1f} s)",
+            "sample": f"fp64 oracle, {heads} query head(s) x last {rows} rows "
+                      f"of the causal N={N} d={d} GQA prefill "
+                      f"({flops / 1e9:.1f} GFLOP in {el:.1f} s)",
             "seconds": el}
 
 
@@ -187,6 +189,13 @@ def main():
             od, ld, ws if need else None, need, 0, stream)
         info["decode"] = dict(bytes=decode_bytes(di, Hkv, d), cfg=c,
                               kv_tokens=int(di.seq_lens.sum()))
+    if "copy" in legs:
+        # plain copy of a known size: reference reading for the HBM counters
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        calls["copy"] = lambda: torch.mul(src, 1.0, out=dst)
+        info["copy"] = dict(bytes=2 * nbytes)
     if "fp8" in legs:
         c = W.PREFILL_CONFIGS[FP8]
         inp = W.prefill_config(FP8)
@@ -201,7 +210,7 @@ def main():
     torch.cuda.synchronize()
     print(f"bench: inputs resident, legs={legs}", file=sys.stderr, flush=True)
 
-    order = [x for x in ("prefill", "decode", "fp8") if x in calls]
+    order = [x for x in ("prefill", "decode", "fp8", "copy") if x in calls]
     for _ in range(args.warmup):
         for name in order:
             calls[name]()
@@ -280,6 +289,13 @@ def main():
                         f"d={c['d']}")
         if "value" not in out:
             out["value"], out["unit"] = tf, "TFLOPS"
+    if "copy" in order:
+        t = statistics.mean(ms["copy"]) / 1e3
+        out["copy_calibration"] = {"bytes_per_launch": info["copy"]["bytes"],
+                                   "GB/s": info["copy"]["bytes"] / t / 1e9,
+                                   "launch_ms_mean": t * 1e3}
+        if "value" not in out:
+            out["value"], out["unit"] = info["copy"]["bytes"] / t / 1e9, "GB/s"
     out["config"] = {"workload": " + ".join(workload), "seed": 42,
                      "parallelism": "single GPU"}
     if not args.no_cpu_baseline and "prefill" in order:

@@ -87,6 +87,20 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float x0, float x1, float x2,
   w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
   return (uint32_t)w;
 }
+// acc + lo + hi of a packed bf16 pair (v_dot2c_f32_bf16 against ones).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
+                                         acc, false);
+}
+// acc + the four e4m3 values of a packed word.
+__device__ __forceinline__ float add_e4m3x4(uint32_t w, float acc) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return acc + ((lo[0] + lo[1]) + (hi[0] + hi[1]));
+}
 
 // ------------------------------------------------ workgroup -> tile map
 // One workgroup computes one BM-row query tile of one (batch, query head).
@@ -119,9 +133,15 @@ __device__ __forceinline__ TileIdx map_tile(int bid, int n_qt, int Hq,
 // ---------------------------------------------- online softmax on S^T
 // State of one query row (one lane, mirrored in lane ^ 32).
 struct RowState {
-  float m;  // exponent reference in log2 units (-inf until a key is seen)
-  float l;  // this lane's partial sum of P (its 16 of every 32 keys)
+  float m;   // exponent reference in log2 units (-inf until a key is seen)
+  float l;   // this lane's partial sum of P (its 16 of every 32 keys), fp32
+  float lr;  // the same sum over P as rounded for the P.V product
 };
+// Why two sums: O is divided by lr, so the weights applied to V are the
+// rounded P divided by their own sum, an exact convex combination (the
+// rounding of P then only perturbs the weights, it cannot scale O);
+// LSE = m + log2(l) uses the unrounded sum. Kernels whose P.V product is
+// fp32 keep lr == l.
 
 // Applies one key tile to the running state ([Capstone §2.2 steps 3-4]
 // with the deferred normalisation of §4.2): s[] holds the raw scores of
@@ -145,6 +165,7 @@ __device__ __forceinline__ void online_softmax_tile(f32x16 (&s)[NKB],
     const float mnew = fmaxf(st.m, mxs);
     const float alpha = (st.m == kNegInf) ? 0.f : fast_exp2(st.m - mnew);
     st.l *= alpha;
+    st.lr *= alpha;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll

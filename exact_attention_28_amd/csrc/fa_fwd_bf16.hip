@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
-  RowState st{kNegInf, 0.f};
+  RowState st{kNegInf, 0.f, 0.f};
 
   // ---- register staging of one K/V tile
   u32x4 kr[T::KLOADS];
@@ -202,8 +202,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int j = 0; j < 2; ++j) {
           uint32_t pw[4];
 #pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2)
+          for (int t2 = 0; t2 < 4; ++t2) {
             pw[t2] = pack_bf16x2(s[kb][8 * j + 2 * t2], s[kb][8 * j + 2 * t2 + 1]);
+            st.lr = add_bf16x2(pw[t2], st.lr);
+          }
           u32x4 pv = {pw[0], pw[1], pw[2], pw[3]};
           const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
 #pragma unroll
@@ -219,11 +221,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue: O = O^T / l, LSE = ln 2 * (m + log2 l)
+  // ---- epilogue: O = O^T / lr, LSE = ln 2 * (m + log2 l)
   const float ltot = st.l + xor_lane(st.l, 32);
+  const float lrtot = st.lr + xor_lane(st.lr, 32);
   if (row < Nq) {
     const bool live = ltot > 0.f;
-    const float inv = live ? 1.f / ltot : 0.f;
+    const float inv = live ? 1.f / lrtot : 0.f;
     __bf16* orow = O + qbase + (long)row * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)

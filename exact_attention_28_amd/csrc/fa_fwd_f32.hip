@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
-  RowState st{kNegInf, 0.f};
+  RowState st{kNegInf, 0.f, 0.f};  // fp32 P.V: lr unused (equals l)
 
   constexpr int C4 = D / 4;  // float4 chunks per row
   for (int t = 0; t < nt; ++t) {

@@ -7,7 +7,8 @@
 // s_q*s_k is folded with scale*log2(e) into the single multiply that turns
 // raw scores into exp2 arguments, and s_v into the final 1/l.
 // P is the unnormalised exp2(s - m_ref) <= 2^kTau = 256 < 448, so it fits
-// e4m3 without a scale; l is summed from the fp32 P.
+// e4m3 without a scale. O is normalised by the sum of the rounded P (an
+// exact convex combination of V rows), LSE uses the sum of the fp32 P.
 //
 // Structure as the bf16 kernel (128-row Q tile, 64-key K/V tiles,
 // double-buffered swizzled LDS, S^T / O^T register layout) on
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
-  RowState st{kNegInf, 0.f};
+  RowState st{kNegInf, 0.f, 0.f};
 
   u32x4 kr[T::KLOADS];
   u32x2 vr[4];
@@ -200,8 +201,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int kb = j >> 2, v0 = 4 * (j & 3);
-        pb[j] = (int)pack_e4m3x4(s[kb][v0], s[kb][v0 + 1], s[kb][v0 + 2],
-                                 s[kb][v0 + 3]);
+        const uint32_t w8 = pack_e4m3x4(s[kb][v0], s[kb][v0 + 1],
+                                        s[kb][v0 + 2], s[kb][v0 + 3]);
+        st.lr = add_e4m3x4(w8, st.lr);
+        pb[j] = (int)w8;
       }
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
@@ -220,9 +223,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   }
 
   const float ltot = st.l + xor_lane(st.l, 32);
+  const float lrtot = st.lr + xor_lane(st.lr, 32);
   if (row < Nq) {
     const bool live = ltot > 0.f;
-    const float inv = live ? s_v / ltot : 0.f;
+    const float inv = live ? s_v / lrtot : 0.f;
     __bf16* orow = O + qbase + (long)row * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
