@@ -67,6 +67,20 @@ __device__ __forceinline__ f32x16 mfma_32x32x64_e4m3(i32x8 a, i32x8 b,
 __device__ __forceinline__ float xor_lane(float x, int mask) {
   return __shfl_xor(x, mask, 64);
 }
+// x[l] and x[l ^ 32] in every lane (v_permlane32_swap: lanes 32-63 of one
+// copy trade places with lanes 0-31 of the other), reduced with max / add.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // ---------------------------------------------------------- conversions
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -158,7 +172,7 @@ __device__ __forceinline__ void online_softmax_tile(f32x16 (&s)[NKB],
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-  mx = fmaxf(mx, xor_lane(mx, 32));
+  mx = max_halves(mx);
   const float mxs = mx * c;  // c > 0, so max commutes with the scaling
   const bool need = mxs > st.m + kTau;
   if (__any(need)) {

@@ -9,13 +9,12 @@
 // ([Capstone §7.3 Q2]); the tiles that cross it are masked per element.
 //
 // Data flow per key tile (double-buffered LDS, one barrier per tile):
-//   global K, V (16 B per lane, coalesced 256 B rows) -> VGPRs (prefetched
-//   one tile ahead, overlapping the MFMA work of the current tile)
-//   -> LDS: K row-major with an XOR swizzle of its 16 B chunks;
-//           V transposed to V^T (d-major) so the PV operand is a single
-//           16 B read, also XOR-swizzled.
+//   global K, V (16 B per lane) -> VGPRs (prefetched one tile ahead,
+//   overlapping the MFMA work of the current tile) -> LDS, both row-major
+//   with padded rows
 //   -> per wave: S^T = K Q^T (Q lives in VGPRs for the whole tile),
-//      online softmax, P^T packed to bf16 in registers, O^T += V^T P^T.
+//      online softmax, P^T packed to bf16 in registers, O^T += V^T P^T with
+//      the V^T operand produced by gfx950's LDS transpose read.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -28,32 +27,28 @@ constexpr int kThreads = 256;  // 4 waves
 
 template <int D>
 struct Bf16Tile {
-  static constexpr int CPR = D / 8;                        // 16 B chunks/row
-  static constexpr int K_BYTES = kBN * D * 2;              // K tile
-  static constexpr int VT_ROW = kBN * 2;                   // V^T row bytes
-  static constexpr int VT_BYTES = D * VT_ROW;              // V^T tile
-  static constexpr int STAGE = K_BYTES + VT_BYTES;
-  static constexpr int KLOADS = kBN * CPR / kThreads;      // 16 B per lane
-  static constexpr int VUNITS = (kBN / 4) * CPR;           // 4 keys x 8 d
+  static constexpr int CPR = D / 8;                   // 16 B chunks per row
+  static constexpr int K_ROW = D * 2 + 16;            // padded K row
+  static constexpr int V_ROW = D * 2 + 64;            // padded V row
+  static constexpr int K_BYTES = kBN * K_ROW;
+  static constexpr int V_BYTES = kBN * V_ROW;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int LOADS = kBN * CPR / kThreads;  // 16 B per lane, each of K, V
+  static constexpr int ROWS_PER_LOAD = kThreads / CPR;
 };
 
-// Physical 16 B chunk of K row `key` that holds logical chunk c: 16
-// consecutive keys reading one logical chunk, and 16 lanes writing one
-// row, both hit 16 distinct 16 B bank groups.
-template <int D>
-__device__ __forceinline__ int k_chunk(int key, int c) {
-  if constexpr (D == 128) return c ^ (key & 15);
-  else return c ^ ((key >> 1) & 7);
-}
-// V^T row d holds 64 keys (8 chunks of 16 B). Reads (16 consecutive d, one
-// chunk) are conflict free; the transposing writes see at most 4-way.
-__device__ __forceinline__ int vt_chunk(int d, int c) {
-  return c ^ (((d >> 1) ^ (d >> 4)) & 7);
-}
-// Inside a V^T row, key k of the tile is stored at position pi(k) = k with
-// bits 2 and 3 swapped: the 8 keys one MFMA lane needs for the PV step
-// (4h + {0..3} and 8 + 4h + {0..3} within a 16-key step) become one 16 B
-// chunk, ordered like the P^T operand taken from the S^T accumulator.
+// LDS layouts (both row-major, rows padded so every fragment address is a
+// per-lane base plus a compile-time offset, and no access conflicts):
+//  * K rows padded by 16 B (stride = 17 groups of 16 B): the S^T = K Q^T
+//    A operand is one 16 B read per lane, 16 consecutive keys at one
+//    chunk -> 16 distinct bank groups.
+//  * V rows padded by 64 B (stride = 16 mod 64 banks): the O^T = V^T P^T A
+//    operand is read with ds_read_b64_tr_b16. In each 16-lane group, lane j
+//    fetches 4 consecutive d of key row kbase + j/4 and the transpose hands
+//    lane i the 4 keys kbase..kbase+3 at column dbase + i -- the k-major
+//    V^T fragment the MFMA needs. A 32-lane half reads 4 rows x 64 B, which
+//    the stride spreads over all 64 banks.
+//  * Writes: 16 lanes store one 256 B row (D = 128) or two 128 B rows.
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
@@ -75,7 +70,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int hk = ti.hq / (Hq / Hkv);
   const int q0 = ti.qt * kBM;
   const long qbase = (long)(ti.b * Hq + ti.hq) * Nq * D;
-  const long kvbase = (long)(ti.b * Hkv + hk) * Nk * D;
+  const __bf16* Kh = K + (long)(ti.b * Hkv + hk) * Nk * D;
+  const __bf16* Vh = V + (long)(ti.b * Hkv + hk) * Nk * D;
   const int off = Nk - Nq;  // bottom-right causal alignment
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, min(q0 + kBM, Nq) + off);
@@ -99,64 +95,56 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
   RowState st{kNegInf, 0.f, 0.f};
 
-  // ---- register staging of one K/V tile
-  u32x4 kr[T::KLOADS];
-  u32x4 vr[4];
-  const int vkg = tid / T::CPR;  // 4-key group of this lane's V unit
-  const int vdc = tid % T::CPR;  // 8-element d chunk of this lane's V unit
+  // ---- K/V tile staging. Lane tid moves chunk (tid % CPR) of rows
+  // tid / CPR + ROWS_PER_LOAD * i. Full tiles use a uniform base plus a
+  // loop-invariant lane offset; on the ragged last tile rows past Nk are
+  // clamped to the last key (their scores are masked, their P is 0).
+  const int lrow = tid / T::CPR;
+  const int lcol = (tid % T::CPR) * 8;
+  u32x4 kr[T::LOADS], vr[T::LOADS];
   auto load_tile = [&](int n0) {
+    const __bf16* kt = Kh + (long)n0 * D;
+    const __bf16* vt = Vh + (long)n0 * D;
+    if (n0 + kBN <= Nk) {
 #pragma unroll
-    for (int i = 0; i < T::KLOADS; ++i) {
-      const int u = tid + kThreads * i;
-      const int key = u / T::CPR, cc = u % T::CPR;
-      const int gk = n0 + key;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kr[i] = gk < Nk ? *reinterpret_cast<const u32x4*>(K + kvbase +
-                                                        (long)gk * D + 8 * cc)
-                      : z;
-    }
-    if (tid < T::VUNITS) {
+      for (int i = 0; i < T::LOADS; ++i) {
+        const int o_ = (lrow + T::ROWS_PER_LOAD * i) * D + lcol;
+        kr[i] = *reinterpret_cast<const u32x4*>(kt + o_);
+        vr[i] = *reinterpret_cast<const u32x4*>(vt + o_);
+      }
+    } else {
+      const int last = Nk - 1 - n0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gk = n0 + 4 * vkg + r;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        vr[r] = gk < Nk ? *reinterpret_cast<const u32x4*>(
-                              V + kvbase + (long)gk * D + 8 * vdc)
-                        : z;
+      for (int i = 0; i < T::LOADS; ++i) {
+        const int o_ = min(lrow + T::ROWS_PER_LOAD * i, last) * D + lcol;
+        kr[i] = *reinterpret_cast<const u32x4*>(kt + o_);
+        vr[i] = *reinterpret_cast<const u32x4*>(vt + o_);
       }
     }
   };
   auto store_tile = [&](int stage) {
-    char* ks = smem + stage * T::STAGE;
-    char* vs = ks + T::K_BYTES;
+    char* ks = smem + stage * T::STAGE + lrow * T::K_ROW + lcol * 2;
+    char* vs = smem + stage * T::STAGE + T::K_BYTES + lrow * T::V_ROW + lcol * 2;
 #pragma unroll
-    for (int i = 0; i < T::KLOADS; ++i) {
-      const int u = tid + kThreads * i;
-      const int key = u / T::CPR, cc = u % T::CPR;
-      *reinterpret_cast<u32x4*>(ks + key * (D * 2) + k_chunk<D>(key, cc) * 16) =
-          kr[i];
-    }
-    if (tid < T::VUNITS) {
-      // keys 4*vkg .. +3 sit at V^T positions pi(4*vkg) .. +3
-      const int cpos = 2 * (vkg >> 2) + (vkg & 1);
-      const int half = (vkg >> 1) & 1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * vdc + e;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 pr;
-        pr[0] = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
-        pr[1] = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
-        *reinterpret_cast<u32x2*>(vs + d * T::VT_ROW + vt_chunk(d, cpos) * 16 +
-                                  half * 8) = pr;
-      }
+    for (int i = 0; i < T::LOADS; ++i) {
+      *reinterpret_cast<u32x4*>(ks + i * T::ROWS_PER_LOAD * T::K_ROW) = kr[i];
+      *reinterpret_cast<u32x4*>(vs + i * T::ROWS_PER_LOAD * T::V_ROW) = vr[i];
     }
   };
+
+  // per-lane LDS bases of the fragment reads
+  const int kfrag = (32 * 0 + r32) * T::K_ROW + 16 * h;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int vfrag = (4 * h + (i16 >> 2)) * T::V_ROW + (16 * (g16 & 1) + 4 * (i16 & 3)) * 2;
 
   if (nt > 0) {
     load_tile(0);
     store_tile(0);
   }
+  // Everything loaded so far (Q fragments, first tile) has landed: inside
+  // the loop the only outstanding global loads are the next tile's, which
+  // nothing reads until it is stored.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
@@ -165,19 +153,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     if (has_next) load_tile(n0 + kBN);
     const bool skip = CAUSAL && (n0 > wrow0 + 31 + off);
     if (!skip) {
-      const char* ks = smem + (t & 1) * T::STAGE;
-      const char* vs = ks + T::K_BYTES;
+      const char* ks = smem + (t & 1) * T::STAGE + kfrag;
+      const char* vs = smem + (t & 1) * T::STAGE + T::K_BYTES + vfrag;
       // S^T = K Q^T for two 32-key blocks
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-        const int key = 32 * kb + r32;
 #pragma unroll
         for (int sd = 0; sd < D / 16; ++sd) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              ks + key * (D * 2) + k_chunk<D>(key, 2 * sd + h) * 16);
+              ks + 32 * kb * T::K_ROW + 32 * sd);
           s[kb] = mfma_32x32x16_bf16(a, qf[sd], s[kb]);
         }
       }
@@ -195,7 +182,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           }
       }
       online_softmax_tile<2, D / 32>(s, o, st, c);
-      // O^T += V^T P^T, 16 keys per MFMA
+      // O^T += V^T P^T, 16 keys per MFMA: lane half h contracts keys
+      // 32kb + 16j + 4h + {0..3} (items 0..3) and +8 (items 4..7)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -210,9 +198,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
 #pragma unroll
           for (int mb = 0; mb < D / 32; ++mb) {
-            const int dd = 32 * mb + r32;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                vs + dd * T::VT_ROW + vt_chunk(dd, 4 * kb + 2 * j + h) * 16);
+            const char* vp = vs + (32 * kb + 16 * j) * T::V_ROW + 64 * mb;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(vp));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(vp + 8 * T::V_ROW));
+            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             o[mb] = mfma_32x32x16_bf16(a, pb, o[mb]);
           }
         }
@@ -222,8 +213,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   }
 
   // ---- epilogue: O = O^T / lr, LSE = ln 2 * (m + log2 l)
-  const float ltot = st.l + xor_lane(st.l, 32);
-  const float lrtot = st.lr + xor_lane(st.lr, 32);
+  const float ltot = sum_halves(st.l);
+  const float lrtot = sum_halves(st.lr);
   if (row < Nq) {
     const bool live = ltot > 0.f;
     const float inv = live ? 1.f / lrtot : 0.f;
