@@ -199,4 +199,58 @@ __device__ __forceinline__ void online_softmax_tile(f32x16 (&s)[NKB],
   st.l += sum;
 }
 
+// The same update split in two, so that a caller can put independent MFMA
+// work between them. softmax_reference: row max of the tile (masked
+// entries -inf), lazy move of the exponent reference, l and lr rescaled;
+// returns the factor O must be multiplied by (1 when the reference did not
+// move). softmax_exp_pack: P = exp2(s*c - m_ref) summed into l, rounded to
+// bf16 and packed in the PV operand order (block kb, 16-key step j, pairs),
+// the rounded values summed into lr.
+template <int NKB>
+__device__ __forceinline__ float softmax_reference(f32x16 (&s)[NKB],
+                                                   RowState& st, float c) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+  mx = max_halves(mx);
+  const float mxs = mx * c;
+  float alpha = 1.f;
+  if (__any(mxs > st.m + kTau)) {
+    const float mnew = fmaxf(st.m, mxs);
+    alpha = (st.m == kNegInf) ? 0.f : fast_exp2(st.m - mnew);
+    st.l *= alpha;
+    st.lr *= alpha;
+    st.m = mnew;
+  }
+  return alpha;
+}
+
+template <int NKB>
+__device__ __forceinline__ void softmax_exp_pack(f32x16 (&s)[NKB],
+                                                 RowState& st, float c,
+                                                 uint32_t (&pw)[NKB][2][4]) {
+  const float mref = (st.m == kNegInf) ? 0.f : st.m;
+  float sum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = fast_exp2(__builtin_fmaf(s[kb][v], c, -mref));
+      s[kb][v] = p;
+      sum += p;
+    }
+  st.l += sum;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) {
+        pw[kb][j][t2] = pack_bf16x2(s[kb][8 * j + 2 * t2], s[kb][8 * j + 2 * t2 + 1]);
+        st.lr = add_bf16x2(pw[kb][j][t2], st.lr);
+      }
+}
+
 }  // namespace fa

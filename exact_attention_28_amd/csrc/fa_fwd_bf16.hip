@@ -25,30 +25,42 @@ constexpr int kBM = 128;       // query rows per workgroup (32 per wave)
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;  // 4 waves
 
+// ------------------------------------------------------------ LDS layout
+// K and V tiles (64 rows x d) arrive by direct global->LDS loads
+// (global_load_lds_dwordx4): one instruction moves 64 lanes x 16 B into 1 KB
+// of contiguous LDS, so a tile is stored as 1 KB blocks of RPB rows, placed
+// at a pitch of 1 KB + 16 B (+ 32 B for V at d = 64). Which rows share a
+// block is chosen so that every fragment read is conflict free and is one
+// per-lane base plus a compile-time offset:
+//  * K: block b holds rows b, b + NB, b + 2NB, ... The S^T = K Q^T A operand
+//    (16 B per lane, 16 consecutive keys at one chunk) then touches 16
+//    different blocks, whose pitch spreads them over the 16 bank groups.
+//  * V: block (r % 4) * NB/4 + r / (4 RPB) holds row r at slot (r/4) % RPB.
+//    The O^T = V^T P^T A operand is read with ds_read_b64_tr_b16: in each
+//    16-lane group lane j fetches 4 consecutive d of key row kbase + j/4 and
+//    the transpose hands lane i the keys kbase..kbase+3 at column dbase + i
+//    (the k-major V^T fragment the MFMA needs). A 32-lane half reads rows
+//    kbase..kbase+3, which sit in blocks 64 B apart modulo 256 B.
 template <int D>
-struct Bf16Tile {
-  static constexpr int CPR = D / 8;                   // 16 B chunks per row
-  static constexpr int K_ROW = D * 2 + 16;            // padded K row
-  static constexpr int V_ROW = D * 2 + 64;            // padded V row
-  static constexpr int K_BYTES = kBN * K_ROW;
-  static constexpr int V_BYTES = kBN * V_ROW;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int LOADS = kBN * CPR / kThreads;  // 16 B per lane, each of K, V
-  static constexpr int ROWS_PER_LOAD = kThreads / CPR;
+struct Lay {
+  static constexpr int CPR = D / 8;             // 16 B chunks per row
+  static constexpr int RPB = 1024 / (2 * D);    // rows per 1 KB block
+  static constexpr int NB = kBN / RPB;          // blocks per tile
+  static constexpr int KPITCH = 1040;
+  static constexpr int VPITCH = D == 128 ? 1040 : 1056;
+  static constexpr int K_BYTES = NB * KPITCH;
+  static constexpr int V_BYTES = NB * VPITCH;
+  static constexpr int BPW = NB / 4;            // blocks each wave loads
 };
 
-// LDS layouts (both row-major, rows padded so every fragment address is a
-// per-lane base plus a compile-time offset, and no access conflicts):
-//  * K rows padded by 16 B (stride = 17 groups of 16 B): the S^T = K Q^T
-//    A operand is one 16 B read per lane, 16 consecutive keys at one
-//    chunk -> 16 distinct bank groups.
-//  * V rows padded by 64 B (stride = 16 mod 64 banks): the O^T = V^T P^T A
-//    operand is read with ds_read_b64_tr_b16. In each 16-lane group, lane j
-//    fetches 4 consecutive d of key row kbase + j/4 and the transpose hands
-//    lane i the 4 keys kbase..kbase+3 at column dbase + i -- the k-major
-//    V^T fragment the MFMA needs. A 32-lane half reads 4 rows x 64 B, which
-//    the stride spreads over all 64 banks.
-//  * Writes: 16 lanes store one 256 B row (D = 128) or two 128 B rows.
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
+                                   16, 0, 0);
+}
+// s_waitcnt vmcnt(0): the direct loads of this wave have reached LDS.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
@@ -56,8 +68,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,
     float c) {
-  using T = Bf16Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  using T = Lay<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::K_BYTES + 2 * T::V_BYTES];
+  lds_char* const kbuf0 = (lds_char*)smem;
+  lds_char* const vbuf0 = kbuf0 + 2 * T::K_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -95,79 +109,102 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
   RowState st{kNegInf, 0.f, 0.f};
 
-  // ---- K/V tile staging. Lane tid moves chunk (tid % CPR) of rows
-  // tid / CPR + ROWS_PER_LOAD * i. Full tiles use a uniform base plus a
-  // loop-invariant lane offset; on the ragged last tile rows past Nk are
-  // clamped to the last key (their scores are masked, their P is 0).
-  const int lrow = tid / T::CPR;
-  const int lcol = (tid % T::CPR) * 8;
-  u32x4 kr[T::LOADS], vr[T::LOADS];
-  auto load_tile = [&](int n0) {
-    const __bf16* kt = Kh + (long)n0 * D;
-    const __bf16* vt = Vh + (long)n0 * D;
+  // ---- direct loads. Wave w fills blocks w, w+4, ...; lane l moves chunk
+  // l % CPR of the block's slot l / CPR. Full tiles use precomputed lane
+  // offsets; on the ragged last tile rows past Nk are clamped to the last
+  // key (their scores are masked, their P is 0).
+  const int slot = lane / T::CPR, chunk = lane % T::CPR;
+  auto k_row = [&](int b) { return b + T::NB * slot; };
+  auto v_row = [&](int b) {
+    return 4 * T::RPB * (b % (T::NB / 4)) + 4 * slot + b / (T::NB / 4);
+  };
+  int koff[T::BPW], voff[T::BPW];
+#pragma unroll
+  for (int i = 0; i < T::BPW; ++i) {
+    koff[i] = k_row(w + 4 * i) * D + 8 * chunk;
+    voff[i] = v_row(w + 4 * i) * D + 8 * chunk;
+  }
+  auto issue_k = [&](int tile, int buf) {
+    const int n0 = tile * kBN;
+    const __bf16* src = Kh + (long)n0 * D;
+    lds_char* dst = kbuf0 + buf * T::K_BYTES + w * T::KPITCH;
     if (n0 + kBN <= Nk) {
 #pragma unroll
-      for (int i = 0; i < T::LOADS; ++i) {
-        const int o_ = (lrow + T::ROWS_PER_LOAD * i) * D + lcol;
-        kr[i] = *reinterpret_cast<const u32x4*>(kt + o_);
-        vr[i] = *reinterpret_cast<const u32x4*>(vt + o_);
-      }
+      for (int i = 0; i < T::BPW; ++i)
+        g2lds_16B(src + koff[i], dst + 4 * i * T::KPITCH);
     } else {
       const int last = Nk - 1 - n0;
 #pragma unroll
-      for (int i = 0; i < T::LOADS; ++i) {
-        const int o_ = min(lrow + T::ROWS_PER_LOAD * i, last) * D + lcol;
-        kr[i] = *reinterpret_cast<const u32x4*>(kt + o_);
-        vr[i] = *reinterpret_cast<const u32x4*>(vt + o_);
-      }
+      for (int i = 0; i < T::BPW; ++i)
+        g2lds_16B(src + min(k_row(w + 4 * i), last) * D + 8 * chunk,
+                  dst + 4 * i * T::KPITCH);
     }
   };
-  auto store_tile = [&](int stage) {
-    char* ks = smem + stage * T::STAGE + lrow * T::K_ROW + lcol * 2;
-    char* vs = smem + stage * T::STAGE + T::K_BYTES + lrow * T::V_ROW + lcol * 2;
+  auto issue_v = [&](int tile, int buf) {
+    const int n0 = tile * kBN;
+    const __bf16* src = Vh + (long)n0 * D;
+    lds_char* dst = vbuf0 + buf * T::V_BYTES + w * T::VPITCH;
+    if (n0 + kBN <= Nk) {
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      *reinterpret_cast<u32x4*>(ks + i * T::ROWS_PER_LOAD * T::K_ROW) = kr[i];
-      *reinterpret_cast<u32x4*>(vs + i * T::ROWS_PER_LOAD * T::V_ROW) = vr[i];
+      for (int i = 0; i < T::BPW; ++i)
+        g2lds_16B(src + voff[i], dst + 4 * i * T::VPITCH);
+    } else {
+      const int last = Nk - 1 - n0;
+#pragma unroll
+      for (int i = 0; i < T::BPW; ++i)
+        g2lds_16B(src + min(v_row(w + 4 * i), last) * D + 8 * chunk,
+                  dst + 4 * i * T::VPITCH);
     }
   };
 
-  // per-lane LDS bases of the fragment reads
-  const int kfrag = (32 * 0 + r32) * T::K_ROW + 16 * h;
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int vfrag = (4 * h + (i16 >> 2)) * T::V_ROW + (16 * (g16 & 1) + 4 * (i16 & 3)) * 2;
+  // ---- per-lane fragment bases
+  const int kfrag = (r32 % T::NB) * T::KPITCH + (r32 / T::NB) * (2 * D) + 16 * h;
+  const int i16 = lane & 15, e_l = i16 >> 2;
+  const int vfrag = e_l * (T::NB / 4) * T::VPITCH + h * (2 * D) +
+                    (16 * ((lane >> 4) & 1) + 4 * (i16 & 3)) * 2;
+  // S^T = K Q^T for the two 32-key blocks of a tile (two independent
+  // accumulation chains, interleaved)
+  auto qk = [&](int buf, f32x16 (&s)[2]) {
+    const lds_char* kp = kbuf0 + buf * T::K_BYTES + kfrag;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+    for (int sd = 0; sd < D / 16; ++sd)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(
+            kp + kb * (32 / T::NB) * (2 * D) + 32 * sd);
+        s[kb] = mfma_32x32x16_bf16(a, qf[sd], s[kb]);
+      }
+  };
+  auto skip_tile = [&](int tile) {
+    return CAUSAL && (tile * kBN > wrow0 + 31 + off);
+  };
 
+  // ---- prologue: K(0), V(0), K(1) in flight; S(0)
   if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
+    issue_k(0, 0);
+    issue_v(0, 0);
+    if (nt > 1) issue_k(1, 1);
   }
-  // Everything loaded so far (Q fragments, first tile) has landed: inside
-  // the loop the only outstanding global loads are the next tile's, which
-  // nothing reads until it is stored.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  f32x16 sc[2];
+  if (nt > 0 && !skip_tile(0)) qk(0, sc);
+  __syncthreads();  // K buffer 0 is refilled below
 
   for (int t = 0; t < nt; ++t) {
     const int n0 = t * kBN;
-    const bool has_next = t + 1 < nt;
-    if (has_next) load_tile(n0 + kBN);
-    const bool skip = CAUSAL && (n0 > wrow0 + 31 + off);
-    if (!skip) {
-      const char* ks = smem + (t & 1) * T::STAGE + kfrag;
-      const char* vs = smem + (t & 1) * T::STAGE + T::K_BYTES + vfrag;
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-        for (int sd = 0; sd < D / 16; ++sd) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              ks + 32 * kb * T::K_ROW + 32 * sd);
-          s[kb] = mfma_32x32x16_bf16(a, qf[sd], s[kb]);
-        }
-      }
+    // K runs two tiles ahead, V one: both target buffers were last read
+    // before the previous barrier.
+    if (t + 2 < nt) issue_k(t + 2, t & 1);
+    if (t + 1 < nt) issue_v(t + 1, (t + 1) & 1);
+    const bool do_t = !skip_tile(t);
+    const bool do_n = (t + 1 < nt) && !skip_tile(t + 1);
+    f32x16 sn[2];
+    if (do_t) {
       // mask the ragged end of the key range and the causal diagonal
       const bool need_mask =
           (n0 + kBN > Nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
@@ -178,37 +215,53 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (key > lim) s[kb][v] = kNegInf;
+            if (key > lim) sc[kb][v] = kNegInf;
           }
       }
-      online_softmax_tile<2, D / 32>(s, o, st, c);
+      const float alpha = softmax_reference<2>(sc, st, c);
+      uint32_t pw[2][2][4];
+      // S(t+1) on the matrix cores while P(t) is formed on the VALU
+      if (do_n) {
+        qk((t + 1) & 1, sn);
+        softmax_exp_pack<2>(sc, st, c, pw);
+      } else {
+        softmax_exp_pack<2>(sc, st, c, pw);
+      }
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[mb][v] *= alpha;
+      }
       // O^T += V^T P^T, 16 keys per MFMA: lane half h contracts keys
       // 32kb + 16j + 4h + {0..3} (items 0..3) and +8 (items 4..7)
+      const lds_char* vp0 = vbuf0 + (t & 1) * T::V_BYTES + vfrag;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          uint32_t pw[4];
-#pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2) {
-            pw[t2] = pack_bf16x2(s[kb][8 * j + 2 * t2], s[kb][8 * j + 2 * t2 + 1]);
-            st.lr = add_bf16x2(pw[t2], st.lr);
-          }
-          u32x4 pv = {pw[0], pw[1], pw[2], pw[3]};
+          u32x4 pv = {pw[kb][j][0], pw[kb][j][1], pw[kb][j][2], pw[kb][j][3]};
           const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
+          const int rb = 32 * kb + 16 * j;              // multiple of 16
+          const int vimm = (rb / (4 * T::RPB)) * T::VPITCH +
+                           ((rb / 4) % T::RPB) * (2 * D);
 #pragma unroll
           for (int mb = 0; mb < D / 32; ++mb) {
-            const char* vp = vs + (32 * kb + 16 * j) * T::V_ROW + 64 * mb;
+            const lds_char* vp = vp0 + vimm + 64 * mb;
             const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (__attribute__((address_space(3))) bf16x4*)(vp));
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4*)(vp + 8 * T::V_ROW));
+                (__attribute__((address_space(3))) bf16x4*)(vp + 2 * (2 * D)));
             const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             o[mb] = mfma_32x32x16_bf16(a, pb, o[mb]);
           }
         }
     }
-    if (has_next) store_tile((t + 1) & 1);
+    if (do_n) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sc[kb] = sn[kb];
+    }
+    wait_vm0();
     __syncthreads();
   }
 
