@@ -67,10 +67,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     __bf16* __restrict__ O, float* __restrict__ LSE, int B) {
   constexpr int DL = D / 16;  // d columns per lane in the PV step
   const int G = Hq / Hkv;
-  const int split = blockIdx.x % nsplit;
-  const int bh = blockIdx.x / nsplit;
-  const int hkv = bh % Hkv;
-  const int b = bh / Hkv;
+  // kv heads fastest: the workgroups that read the head slices of the same
+  // pages are dispatched together, so each page (all heads of 16 tokens,
+  // contiguous in the pool) is streamed from HBM in one pass
+  const int hkv = blockIdx.x % Hkv;
+  const int rest = blockIdx.x / Hkv;
+  const int split = rest % nsplit;
+  const int b = rest / nsplit;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;

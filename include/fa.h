@@ -155,6 +155,10 @@ size_t fa_paged_decode_workspace_size(int B, int Hq, int Hkv, int d,
  *              aligned; may be NULL when that size is 0. Its contents on
  *              entry do not matter. Two calls that run concurrently must
  *              not share a workspace.
+ * workspace_bytes  the true size of the buffer `workspace` points to. The
+ *              library checks it against the size it needs and cannot check
+ *              it against the allocation: a value larger than the buffer
+ *              lets the kernels write past its end.
  * num_splits   0 = auto, else the number of chunks per request.
  * stream       hipStream_t or NULL.
  */
