@@ -181,12 +181,12 @@ def main():
         npages, page, Hkv, _ = kp.shape
         maxp = bt.shape[1]
         need = fa.fa_paged_decode_workspace_size(B, Hq, Hkv, d, maxp, page, 0)
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
         od = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
         ld = torch.empty((B, Hq), dtype=torch.float32, device=dev)
         calls["decode"] = lambda: fa.fa_paged_decode(
             q, kp, vp, bt, sl, page, npages, B, Hq, Hkv, d, maxp, di.scale,
-            od, ld, ws if need else None, need, 0, stream)
+            od, ld, ws, ws.numel(), 0, stream)
         info["decode"] = dict(bytes=decode_bytes(di, Hkv, d), cfg=c,
                               kv_tokens=int(di.seq_lens.sum()))
     if "copy" in legs:

@@ -54,12 +54,12 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, scale=None,
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     need = _lib.fa_paged_decode_workspace_size(B, Hq, Hkv, d, max_pages,
                                                page_size, num_splits)
-    if need and (workspace is None or
-                 workspace.numel() * workspace.element_size() < need):
+    if (workspace is None or
+            workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wbytes = workspace.numel() * workspace.element_size() if need else 0
     _lib.fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, page_size,
                          num_pages, B, Hq, Hkv, d, max_pages, scale, out,
-                         lse, workspace if need else None, wbytes, num_splits,
-                         stream)
+                         lse, workspace,
+                         workspace.numel() * workspace.element_size(),
+                         num_splits, stream)
     return out, lse

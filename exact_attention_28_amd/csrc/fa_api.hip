@@ -13,6 +13,7 @@
 namespace {
 
 constexpr long kMaxIndex = 0x7fffffffL;  // 32-bit element offsets per head
+constexpr int kMaxRanges = 65536;        // decode page ranges per KV head
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -46,7 +47,7 @@ const char* fa_strerror(int code) {
     case FA_ESCALE: return "softmax scale must be finite and > 0";
     case FA_EPAGE: return "page_size must be 16 and num_pages >= 1";
     case FA_EWORKSPACE: return "workspace missing, misaligned or too small";
-    case FA_ESPLITS: return "num_splits is negative or leaves more than 256 pages per split";
+    case FA_ESPLITS: return "num_splits is negative or above 65536";
     case FA_EALIGN: return "a tensor pointer is not 16-byte aligned";
     default: break;
   }
@@ -120,9 +121,10 @@ static int decode_check(int B, int Hq, int Hkv, int d, int max_pages,
   if (d != 64 && d != 128) return FA_EUNSUPPORTED_D;
   if (Hq % Hkv != 0 || Hq / Hkv > 16) return FA_EGQA;
   if (page_size != 16) return FA_EPAGE;
-  if (num_splits < 0) return FA_ESPLITS;
+  if (num_splits < 0 || num_splits > kMaxRanges) return FA_ESPLITS;
   if ((long)max_pages * page_size > kMaxIndex) return FA_EINVAL_DIM;
   if ((long)B * Hq > kMaxIndex / 256) return FA_EINVAL_DIM;
+  if ((long)B * max_pages > kMaxIndex) return FA_EINVAL_DIM;
   return FA_OK;
 }
 
@@ -159,9 +161,8 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
   fa::DecodePlan plan;
   if (!fa::plan_decode(B, Hq, Hkv, d, max_pages_per_seq, num_splits, &plan))
     return FA_ESPLITS;
-  if (plan.workspace_bytes > 0 &&
-      (!workspace || workspace_bytes < plan.workspace_bytes ||
-       ((uintptr_t)workspace & 255u) != 0))
+  if (!workspace || workspace_bytes < plan.workspace_bytes ||
+      ((uintptr_t)workspace & 255u) != 0)
     return FA_EWORKSPACE;
 
   fa::DecodeArgs a;
@@ -179,11 +180,9 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
   a.scale = scale;
   a.o = o;
   a.lse = lse;
-  a.ws = static_cast<float*>(plan.workspace_bytes > 0 ? workspace : nullptr);
-  a.pages_per_split = plan.pages_per_split;
-  a.num_splits = plan.num_splits;
+  a.ws = workspace;
   a.stream = static_cast<hipStream_t>(stream);
-  return (int)fa::launch_paged_decode(a);
+  return (int)fa::launch_paged_decode(a, plan);
 }
 
 }  // extern "C"

@@ -1,28 +1,37 @@
 // fa_decode.hip - paged-KV-cache decode (one query token per request), gfx950.
 //
 // The cache of each request lives in 16-token pages mapped by a block table
-// ([FA3-paged §3.2]). The work of one request and one KV head is cut into
-// chunks of `pages_per_split` pages; every chunk is a workgroup that
-// streams its pages once from HBM (this kernel is bandwidth bound: every
-// K/V byte is used once, by the Hq/Hkv query heads of the group together)
-// and produces a normalised partial output and its log-sum-exp. A second
-// small kernel merges the partials with the log-sum-exp form of the
-// two-block merge ([Capstone §2.2 step 4], appendix A Q1).
+// ([FA3-paged §3.2]). This kernel is bandwidth bound: every K/V byte is read
+// once from HBM and used by the Hq/Hkv query heads of its group together.
 //
-// Per wave and page (16 tokens, one KV head: 16 rows of d bf16 at a
-// stride of Hkv*d):
+// Work split (balanced split-KV). The pages of the whole batch, request
+// after request, form one list of T pages; it is cut into R ranges of equal
+// length (R about the number of waves the GPU holds at once, divided by
+// Hkv). One wave owns one (range, KV head): it walks the range's pages in
+// order, with K/V loads two pages ahead of the page it computes, and every
+// time it leaves a request (or the range ends) it emits that request's
+// piece. A piece that is a whole request is written as the final output; a
+// piece of a request cut by a range border is written as a normalised
+// partial with its log-sum-exp, and a small second kernel merges those with
+// the log-sum-exp form of the two-block merge ([Capstone §2.2 step 4],
+// appendix A Q1). Ranges never depend on request lengths, so long and short
+// requests cost the same per page and the grid finishes together.
+//
+// The waves of one workgroup hold different KV heads of the same range, so
+// a workgroup of Hkv waves walks the same pages in lockstep and reads each
+// page (all heads of 16 tokens, contiguous in the pool) as one block.
+//
+// Per wave and page (16 tokens of one KV head, rows of d bf16 at a stride of
+// Hkv*d):
 //   * S^T[token, head] = K . Q^T on v_mfma_f32_16x16x32_bf16, with K
 //     fragments loaded straight from HBM into the A operand (lane: token
 //     l%16, 16 B of d) and the group's query heads as the B operand
 //     (lane: head l%16; heads past the group are zero);
 //   * online softmax per head (column): lane-local over 4 tokens, then two
-//     cross-row steps;
+//     cross-row steps, with the lazy rescale of the prefill kernels;
 //   * O[head, d] += P V on the VALU: a lane owns 4 tokens and D/16 d
 //     columns, P is broadcast inside each 16-lane row with DPP
 //     row_newbcast, V is read 16 B per lane from HBM.
-// Pages are assigned round-robin to the 4 waves; the next page's K and V
-// loads are issued before the current page is computed. The waves' states
-// are merged through LDS at the end of the chunk.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -30,8 +39,47 @@ namespace fa {
 namespace {
 
 constexpr int kPage = 16;
-constexpr int kThreads = 256;
-constexpr int kMaxPps = 256;  // pages per split held in LDS
+
+// Workspace layout, in 4-byte words: T at word 0; the first and the last
+// range that touch request b at kFirstWord + b and kFirstWord + B + b; then
+// the partial outputs [(B + R) * Hq][D] fp32 and their log-sum-exps
+// [(B + R) * Hq]. A piece of request b in range r has slot b + r: along the
+// page list (request, range) pairs only grow, so slots never collide.
+constexpr int kFirstWord = 64;
+
+// Sizes and plan; the pointers are kernel arguments of their own, declared
+// __restrict__, so the block table and lengths are read with scalar loads.
+struct KParams {
+  int num_pages, B, Hq, Hkv, G, Hh, WPH, ngroups, max_pages, R;
+  float c;  // scale * log2(e)
+};
+
+__device__ __forceinline__ int pages_of(int len, int max_len) {
+  len = max(0, min(len, max_len));
+  return (len + kPage - 1) / kPage;
+}
+__device__ __forceinline__ int clamp_len(int len, int max_len) {
+  return max(0, min(len, max_len));
+}
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ int uniform(int x) {
+  return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
 
 // Lane n of every 16-lane row, broadcast to the whole row (DPP
 // row_newbcast): P of head n for the four tokens this row holds.
@@ -58,110 +106,99 @@ struct PvAccumulate<0, GP, DL> {
                                              const float (&)[DL]) {}
 };
 
-template <int D, int GP>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
-    const __bf16* __restrict__ Qp, const __bf16* __restrict__ KP,
+template <int D, int GP, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(
+    KParams a, const __bf16* __restrict__ Qp, const __bf16* __restrict__ KP,
     const __bf16* __restrict__ VP, const int32_t* __restrict__ BT,
-    const int32_t* __restrict__ SL, int num_pages, int Hq, int Hkv,
-    int max_pages, int pps, int nsplit, float c, float* __restrict__ ws,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int B) {
+    const int32_t* __restrict__ SL, int* __restrict__ wsi,
+    float* __restrict__ ws_o, float* __restrict__ ws_l,
+    __bf16* __restrict__ O, float* __restrict__ LSE) {
   constexpr int DL = D / 16;  // d columns per lane in the PV step
-  const int G = Hq / Hkv;
-  // kv heads fastest: the workgroups that read the head slices of the same
-  // pages are dispatched together, so each page (all heads of 16 tokens,
-  // contiguous in the pool) is streamed from HBM in one pass
-  const int hkv = blockIdx.x % Hkv;
-  const int rest = blockIdx.x / Hkv;
-  const int split = rest % nsplit;
-  const int b = rest / nsplit;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
+  typedef uint32_t vload_t __attribute__((ext_vector_type(DL / 2)));
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
   const int row16 = lane >> 4;
   const int col = lane & 15;
+  const int hg = blockIdx.x % a.ngroups;
+  const int slot = blockIdx.x / a.ngroups;
+  const int hl = w % a.Hh;
+  const int sub = w / a.Hh;
+  if (sub >= a.WPH) return;
+  const int r = slot * a.WPH + sub;
+  if (r >= a.R) return;
+  const int hkv = hg * a.Hh + hl;
+  const int G = a.G;
+  const int max_len = a.max_pages * kPage;
+  const long tok_stride = (long)a.Hkv * D;  // elements between tokens
 
-  int L = SL[b];
-  L = max(0, min(L, max_pages * kPage));
-  const int npg = (L + kPage - 1) / kPage;
-  const int p0 = split * pps;
-  const int p1 = min(p0 + pps, npg);
-  if (nsplit > 1 && p0 >= p1) return;  // no pages: the merge skips it
-
-  __shared__ int pid[kMaxPps];
-  __shared__ int bad;
-  __shared__ float red_m[4][GP];
-  __shared__ float red_l[4][GP];
-  __shared__ __attribute__((aligned(16))) float red_o[4][GP][D];
-  if (tid == 0) bad = 0;
-  __syncthreads();
-  for (int i = tid; i < p1 - p0; i += kThreads) {
-    int id = BT[(long)b * max_pages + p0 + i];
-    if (id < 0 || id >= num_pages) {
-      bad = 1;  // never dereferenced; the request's output becomes NaN
-      id = 0;
-    }
-    pid[i] = id;
+  // ---- this wave's range [x0, x1) of the batch's page list
+  int T = 0;
+  for (int c0 = 0; c0 < a.B; c0 += 64) {
+    const int i = c0 + lane;
+    T += wave_sum(i < a.B ? pages_of(SL[i], max_len) : 0);
   }
-  __syncthreads();
+  T = uniform(T);
+  if (blockIdx.x == 0 && w == 0 && lane == 0) wsi[0] = T;
+  const int x0 = (int)((long)r * T / a.R);
+  const int x1 = (int)((long)(r + 1) * T / a.R);
+  if (x0 >= x1) return;
 
-  // query heads of the group as the B operand: head col, d = 32s + 8*row16
-  bf16x8 qf[D / 32];
+  // request holding page x0 and the list index of its first page
+  int b0 = 0, s0 = 0;
   {
-    const bool qv = col < G;
-    const __bf16* qrow = Qp + ((long)b * Hq + (long)hkv * G + (qv ? col : 0)) * D;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * row16);
-      if (!qv) x = bf16x8{};
-      qf[s] = x;
+    int S = 0;
+    for (int c0 = 0; c0 < a.B; c0 += 64) {
+      const int i = c0 + lane;
+      const int n = i < a.B ? pages_of(SL[i], max_len) : 0;
+      const int incl = S + wave_incl_scan(n, lane);
+      const unsigned long long hit = __ballot(incl > x0);
+      if (hit != 0ull) {
+        const int f = uniform(__builtin_ctzll(hit));
+        b0 = c0 + f;
+        s0 = __builtin_amdgcn_readlane(incl - n, f);
+        break;
+      }
+      S = __builtin_amdgcn_readlane(incl, 63);
     }
   }
 
-  const long tok_stride = (long)Hkv * D;  // elements between tokens
-  float m = kNegInf;                       // reference of head `col`
-  float lp = 0.f;                          // partial sum: head col, 4 tokens
-  float o[GP][DL];
-#pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int e = 0; e < DL; ++e) o[g][e] = 0.f;
-
-  typedef uint32_t vload_t __attribute__((ext_vector_type(DL / 2)));
-  bf16x8 kf[D / 32], kn[D / 32];
-  vload_t vv[4], vn[4];
-  auto load_page = [&](int p, bf16x8 (&kd)[D / 32], vload_t (&vd)[4]) {
-    const long base = ((long)pid[p - p0] * kPage * Hkv + hkv) * D;
+  auto page_base = [&](int id, bool& bad) -> long {
+    bad = id < 0 || id >= a.num_pages;  // never dereferenced: piece -> NaN
+    if (bad) id = 0;
+    return ((long)id * kPage * a.Hkv + hkv) * D;
+  };
+  auto load_page = [&](long base, bf16x8 (&kd)[D / 32], vload_t (&vd)[4]) {
     const __bf16* kp = KP + base + (long)col * tok_stride + 8 * row16;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
       kd[s] = *reinterpret_cast<const bf16x8*>(kp + 32 * s);
     const __bf16* vp = VP + base + (long)(4 * row16) * tok_stride + DL * col;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      vd[r] = *reinterpret_cast<const vload_t*>(vp + r * tok_stride);
+    for (int rr = 0; rr < 4; ++rr)
+      vd[rr] = *reinterpret_cast<const vload_t*>(vp + rr * tok_stride);
   };
 
-  int p = p0 + w;
-  if (p < p1) load_page(p, kn, vn);
-  for (; p < p1; p += 4) {
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) kf[s] = kn[s];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vv[r] = vn[r];
-    if (p + 4 < p1) load_page(p + 4, kn, vn);
+  // query heads of the group as the B operand: head col, d = 32s + 8*row16
+  bf16x8 qf[D / 32];
+  float m, lp;  // exponent reference of head `col`; its partial sum
+  float o[GP][DL];
+  bool piece_bad;
 
+  auto process = [&](const bf16x8 (&kf)[D / 32], const vload_t (&vv)[4],
+                     bool bad, int page, int lim) {
+    piece_bad |= bad;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) acc = mfma_16x16x32_bf16(kf[s], qf[s], acc);
     // lane: tokens 4*row16 + v of this page, head col
-    const int tok0 = p * kPage + 4 * row16;
+    const int tok0 = page * kPage + 4 * row16;
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      if (tok0 + v >= L) acc[v] = kNegInf;
+      if (tok0 + v >= lim) acc[v] = kNegInf;
     float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     mx = fmaxf(mx, xor_lane(mx, 16));
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    const float mxs = mx * c;
+    mx = max_halves(mx);
+    const float mxs = mx * a.c;
     const bool need = (col < G) && (mxs > m + kTau);
     if (__any(need)) {
       const float mnew = fmaxf(m, mxs);
@@ -170,8 +207,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       m = mnew;
 #pragma unroll
       for (int g = 0; g < GP; ++g) {
-        const float ag = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(alpha), g));
+        const float ag = lane_value(alpha, g);
 #pragma unroll
         for (int e = 0; e < DL; ++e) o[g][e] *= ag;
       }
@@ -180,108 +216,181 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     float pr[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      pr[v] = fast_exp2(__builtin_fmaf(acc[v], c, -mref));
+      pr[v] = fast_exp2(__builtin_fmaf(acc[v], a.c, -mref));
       lp += pr[v];
     }
     // O[g, d] += sum over this lane's 4 tokens of P[token, g] * V[token, d]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int rr = 0; rr < 4; ++rr) {
       float vf[DL];
 #pragma unroll
       for (int e = 0; e < DL / 2; ++e) {
-        vf[2 * e] = bf16_lo(vv[r][e]);
-        vf[2 * e + 1] = bf16_hi(vv[r][e]);
+        vf[2 * e] = bf16_lo(vv[rr][e]);
+        vf[2 * e + 1] = bf16_hi(vv[rr][e]);
       }
-      PvAccumulate<GP, GP, DL>::run(o, pr[r], vf);
+      PvAccumulate<GP, GP, DL>::run(o, pr[rr], vf);
     }
-  }
+  };
 
-  // ---- reduce the four 16-lane rows, then the four waves through LDS
+  // Pieces: the part of request b inside this range, pages [p, pe).
+  bf16x8 kA[D / 32], kB[D / 32];
+  vload_t vA[4], vB[4];
+  int b = b0, p = x0 - s0, x = x0;
+  for (;;) {
+    const int L = clamp_len(SL[b], max_len);
+    const int n = (L + kPage - 1) / kPage;
+    const int pe = min(n, p + (x1 - x));
+    if (pe <= p) break;  // only if the lengths changed during the call
+    const int lim = min(L, pe * kPage);  // tokens past the piece are masked
+    const int32_t* row = BT + (long)b * a.max_pages;
+    {
+      const bool qv = col < G;
+      const __bf16* qrow =
+          Qp + ((long)b * a.Hq + (long)hkv * G + (qv ? col : 0)) * D;
 #pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int e = 0; e < DL; ++e) {
-      float x = o[g][e];
-      x += xor_lane(x, 16);
-      x += xor_lane(x, 32);
-      o[g][e] = x;
+      for (int s = 0; s < D / 32; ++s) {
+        bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * row16);
+        if (!qv) q8 = bf16x8{};
+        qf[s] = q8;
+      }
     }
-  lp += xor_lane(lp, 16);
-  lp += xor_lane(lp, 32);
-  if (row16 == 0) {
-    if (col < GP) {
-      red_m[w][col] = m;
-      red_l[w][col] = lp;
-    }
+    m = kNegInf;
+    lp = 0.f;
 #pragma unroll
     for (int g = 0; g < GP; ++g)
 #pragma unroll
-      for (int e = 0; e < DL; ++e) red_o[w][g][DL * col + e] = o[g][e];
-  }
-  __syncthreads();
+      for (int e = 0; e < DL; ++e) o[g][e] = 0.f;
+    piece_bad = false;
 
-  const bool poisoned = bad != 0;
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D, d = idx - g * D;
-    float M = kNegInf;
+    // Two page slots, each reloaded right after it is computed. Loads past
+    // the piece repeat its last page (cached, never used); an odd piece
+    // ends with slot B on such a page, fully masked.
+    // The prologue issues Q, slot A, slot B in that order (the barriers pin
+    // it), the same order the loop leaves behind, so the waits at the loop
+    // head count only slot A's loads.
+    bool badA, badB;
+    __builtin_amdgcn_sched_barrier(0);
+    load_page(page_base(row[p], badA), kA, vA);
+    __builtin_amdgcn_sched_barrier(0);
+    load_page(page_base(row[min(p + 1, pe - 1)], badB), kB, vB);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int q = p; q < pe; q += 2) {
+      const int idA = row[min(q + 2, pe - 1)];
+      const int idB = row[min(q + 3, pe - 1)];
+      process(kA, vA, badA, q, lim);
+      // keep each reload after the last read of its slot
+      __builtin_amdgcn_sched_barrier(0);
+      load_page(page_base(idA, badA), kA, vA);
+      process(kB, vB, badB, q + 1, lim);
+      __builtin_amdgcn_sched_barrier(0);
+      load_page(page_base(idB, badB), kB, vB);
+    }
+
+    // Emit the piece: final output when it is the whole request, else a
+    // partial in slot b + r.
+    const bool first = p == 0, req_end = pe == n;
+    const bool whole = first && req_end;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red_m[ww][g]);
-    float os = 0.f, ls = kNegInf;
-    if (M != kNegInf) {
-      float wl = 0.f, wo = 0.f;
+    for (int g = 0; g < GP; ++g)
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float f = fast_exp2(red_m[ww][g] - M);
-        wl += f * red_l[ww][g];
-        wo += f * red_o[ww][g][d];
+      for (int e = 0; e < DL; ++e) {
+        float t = o[g][e];
+        t += xor_lane(t, 16);
+        t += xor_lane(t, 32);
+        o[g][e] = t;
       }
-      os = wo / wl;
-      ls = (M + fast_log2(wl)) * kLn2;
+    float ls = lp + xor_lane(lp, 16);
+    ls += xor_lane(ls, 32);
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      if (g >= G) continue;
+      const float mg = lane_value(m, g);
+      const float lg = lane_value(ls, g);
+      const bool live = lg > 0.f;
+      float inv = live ? 1.f / lg : 0.f;
+      float lse = live ? (mg + fast_log2(lg)) * kLn2 : kNegInf;
+      if (piece_bad) {
+        inv = __builtin_nanf("");
+        lse = __builtin_nanf("");
+      }
+      if (row16 == (g & 3)) {
+        const long hq = (long)b * a.Hq + (long)hkv * G + g;
+        if (whole) {
+          vload_t st;
+#pragma unroll
+          for (int e = 0; e < DL / 2; ++e)
+            st[e] = pack_bf16x2(o[g][2 * e] * inv, o[g][2 * e + 1] * inv);
+          *reinterpret_cast<vload_t*>(O + hq * D + DL * col) = st;
+          if (col == 0 && LSE != nullptr) LSE[hq] = lse;
+        } else {
+          const long ph = ((long)b + r) * a.Hq + (long)hkv * G + g;
+          float* po = ws_o + ph * D + DL * col;
+#pragma unroll
+          for (int e = 0; e < DL; e += 4) {
+            f32x4 t = {o[g][e] * inv, o[g][e + 1] * inv, o[g][e + 2] * inv,
+                       o[g][e + 3] * inv};
+            *reinterpret_cast<f32x4*>(po + e) = t;
+          }
+          if (col == 0) ws_l[ph] = lse;
+        }
+      }
     }
-    if (poisoned) {
-      os = __builtin_nanf("");
-      ls = __builtin_nanf("");
+    if (hkv == 0 && lane == 0) {
+      if (first) wsi[kFirstWord + b] = r;
+      if (req_end) wsi[kFirstWord + a.B + b] = r;
     }
-    const long hq = (long)b * Hq + (long)hkv * G + g;
-    if (nsplit > 1) {
-      ws[(hq * nsplit + split) * D + d] = os;
-      if (d == 0) ws[(long)B * Hq * nsplit * D + hq * nsplit + split] = ls;
-    } else {
-      O[hq * D + d] = (__bf16)os;
-      if (d == 0 && LSE != nullptr) LSE[hq] = ls;
-    }
+
+    x += pe - p;
+    if (x >= x1) break;
+    do {
+      ++b;
+    } while (b + 1 < a.B && pages_of(SL[b], max_len) == 0);
+    p = 0;
   }
 }
 
-// One workgroup per (request, query head): merge the live splits.
+// One workgroup per (request, query head): merge the pieces of requests
+// that a range border cut; write O = 0, LSE = -inf for empty requests.
 template <int D>
-__global__ __launch_bounds__(128) void decode_merge_kernel(
-    const float* __restrict__ ws, const int32_t* __restrict__ SL,
-    int max_pages, int pps, int nsplit, int Hq, int B,
-    __bf16* __restrict__ O, float* __restrict__ LSE) {
+__global__ __launch_bounds__(D) void decode_merge_kernel(
+    const int* __restrict__ wsi, const float* __restrict__ ws_o,
+    const float* __restrict__ ws_l, const int32_t* __restrict__ SL,
+    int max_pages, int R, int Hq, int B, __bf16* __restrict__ O,
+    float* __restrict__ LSE) {
   const int hq = blockIdx.x;  // b * Hq + h
   const int b = hq / Hq;
-  int L = SL[b];
-  L = max(0, min(L, max_pages * kPage));
-  const int npg = (L + kPage - 1) / kPage;
-  const int ns = (npg + pps - 1) / pps;
-  const float* lse_p = ws + (long)B * Hq * nsplit * D + (long)hq * nsplit;
-  const float* o_p = ws + (long)hq * nsplit * D;
+  const int d = threadIdx.x;
+  const int npg = pages_of(SL[b], max_pages * kPage);
+  if (npg == 0) {
+    O[(long)hq * D + d] = (__bf16)0.f;
+    if (d == 0 && LSE != nullptr) LSE[hq] = kNegInf;
+    return;
+  }
+  const int r_first = wsi[kFirstWord + b];
+  const int r_last = wsi[kFirstWord + B + b];
+  if (r_first == r_last) return;  // one piece: written as the final output
+  const long T = wsi[0];
+  // ranges strictly inside [r_first, r_last] may be empty (T < R)
+  auto live = [&](int r) {
+    return (long)r * T / R < (long)(r + 1) * T / R;
+  };
   float M = kNegInf;
   bool nan = false;
-  for (int s = 0; s < ns; ++s) {
-    const float x = lse_p[s];
+  for (int r = r_first; r <= r_last; ++r) {
+    if (!live(r)) continue;
+    const float x = ws_l[((long)b + r) * Hq + (hq - (long)b * Hq)];
     nan |= (x != x);
     M = fmaxf(M, x);
   }
-  const int d = threadIdx.x;
   float od = 0.f, L_out = kNegInf;
   if (M != kNegInf) {
     float tot = 0.f, acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float f = fast_exp2((lse_p[s] - M) * kLog2e);
+    for (int r = r_first; r <= r_last; ++r) {
+      if (!live(r)) continue;
+      const long ph = ((long)b + r) * Hq + (hq - (long)b * Hq);
+      const float f = fast_exp2((ws_l[ph] - M) * kLog2e);
       tot += f;
-      if (d < D) acc += f * o_p[(long)s * D + d];
+      acc += f * ws_o[ph * D + d];
     }
     od = acc / tot;
     L_out = M + fast_log2(tot) * kLn2;
@@ -290,74 +399,120 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(
     od = __builtin_nanf("");
     L_out = __builtin_nanf("");
   }
-  if (d < D) O[(long)hq * D + d] = (__bf16)od;
+  O[(long)hq * D + d] = (__bf16)od;
   if (d == 0 && LSE != nullptr) LSE[hq] = L_out;
 }
 
-template <int D, int GP>
-hipError_t launch_split(const DecodeArgs& a) {
-  const long blocks = (long)a.B * a.Hkv * a.num_splits;
-  hipLaunchKernelGGL((decode_split_kernel<D, GP>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, a.stream,
-                     static_cast<const __bf16*>(a.q),
-                     static_cast<const __bf16*>(a.k_pool),
-                     static_cast<const __bf16*>(a.v_pool), a.block_table,
-                     a.seq_lens, a.num_pages, a.Hq, a.Hkv, a.max_pages,
-                     a.pages_per_split, a.num_splits, a.scale * kLog2e, a.ws,
-                     static_cast<__bf16*>(a.o), a.lse, a.B);
-  return hipGetLastError();
+template <int D, int GP, int NW>
+void* kernel_ptr() {
+  return reinterpret_cast<void*>(&decode_kernel<D, GP, NW>);
 }
 
-template <int D>
-hipError_t launch_d(const DecodeArgs& a) {
-  const int G = a.Hq / a.Hkv;
-  hipError_t e;
-  if (G <= 1) e = launch_split<D, 1>(a);
-  else if (G <= 2) e = launch_split<D, 2>(a);
-  else if (G <= 4) e = launch_split<D, 4>(a);
-  else if (G <= 8) e = launch_split<D, 8>(a);
-  else e = launch_split<D, 16>(a);
-  if (e != hipSuccess || a.num_splits == 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(a.B * a.Hq)),
-                     dim3(128), 0, a.stream, a.ws, a.seq_lens, a.max_pages,
-                     a.pages_per_split, a.num_splits, a.Hq, a.B,
-                     static_cast<__bf16*>(a.o), a.lse);
-  return hipGetLastError();
+// Kernel instance for head dim d, group size G and waves per workgroup nw.
+void* select_kernel(int d, int G, int nw) {
+#define FA_PICK8(DD, NWW)                                         \
+  if (G <= 1) return kernel_ptr<DD, 1, NWW>();                    \
+  if (G <= 2) return kernel_ptr<DD, 2, NWW>();                    \
+  if (G <= 4) return kernel_ptr<DD, 4, NWW>();                    \
+  return kernel_ptr<DD, 8, NWW>();
+  // eight-wave workgroups are planned only for groups of <= 8 heads
+  if (d == 128) {
+    if (nw == 8) { FA_PICK8(128, 8) }
+    if (G > 8) return kernel_ptr<128, 16, 4>();
+    FA_PICK8(128, 4)
+  }
+  if (nw == 8) { FA_PICK8(64, 8) }
+  if (G > 8) return kernel_ptr<64, 16, 4>();
+  FA_PICK8(64, 4)
+#undef FA_PICK8
+}
+
+// Waves the current device holds at once for this kernel instance.
+int resident_waves(void* kernel, int nw) {
+  int dev = 0, cus = 256, blocks = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &blocks, reinterpret_cast<const void*>(kernel), nw * 64, 0) !=
+          hipSuccess ||
+      blocks <= 0)
+    blocks = 1;
+  return cus * blocks * nw;
 }
 
 }  // namespace
 
 bool plan_decode(int B, int Hq, int Hkv, int d, int max_pages, int num_splits,
-                 DecodePlan* plan) {
-  int pps;
+                 DecodePlan* p) {
+  const int G = Hq / Hkv;
+  const int nw = (Hkv % 8 == 0 && G <= 8) ? 8 : 4;
+  // heads per workgroup: the divisor of Hkv <= nw that keeps most waves busy
+  int hh = 1;
+  for (int c = 1; c <= nw; ++c)
+    if (Hkv % c == 0 && c * (nw / c) >= hh * (nw / hh)) hh = c;
+  p->nw = nw;
+  p->heads_per_wg = hh;
+  p->waves_per_head = nw / hh;
+  p->head_groups = Hkv / hh;
+  long R;
   if (num_splits > 0) {
-    pps = (max_pages + num_splits - 1) / num_splits;
-    if (pps > kMaxPps) return false;
+    R = num_splits;
   } else {
-    // Enough workgroups to keep every CU streaming (>= 8192 chunks incl.
-    // the empty tails of short requests), pages per chunk a power of two.
-    pps = 4;
-    for (int cand = 64; cand >= 4; cand >>= 1) {
-      const long units = (long)B * Hkv * ((max_pages + cand - 1) / cand);
-      if (units >= 8192) {
-        pps = cand;
-        break;
-      }
-    }
+    const int waves = resident_waves(select_kernel(d, G, nw), nw);
+    R = waves / Hkv;
   }
-  if (pps < 1) pps = 1;
-  if (pps > max_pages) pps = max_pages;
-  const int ns = (max_pages + pps - 1) / pps;
-  plan->pages_per_split = pps;
-  plan->num_splits = ns;
-  plan->workspace_bytes =
-      ns > 1 ? (size_t)B * Hq * ns * ((size_t)d + 1) * sizeof(float) : 0;
+  R = ((R + p->waves_per_head - 1) / p->waves_per_head) * p->waves_per_head;
+  if (R < 1) R = 1;
+  p->ranges = (int)R;
+  p->grid = p->head_groups * (long)(R / p->waves_per_head);
+  const long first = kFirstWord + 2L * B;
+  p->off_o = (first + 63) / 64 * 64;
+  p->off_l = p->off_o + ((long)B + R) * Hq * d;
+  p->workspace_bytes = (size_t)(p->off_l + ((long)B + R) * Hq) * 4;
   return true;
 }
 
-hipError_t launch_paged_decode(const DecodeArgs& a) {
-  if (a.d == 128) return launch_d<128>(a);
-  return launch_d<64>(a);
+hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p) {
+  KParams k;
+  k.num_pages = a.num_pages;
+  k.B = a.B;
+  k.Hq = a.Hq;
+  k.Hkv = a.Hkv;
+  k.G = a.Hq / a.Hkv;
+  k.Hh = p.heads_per_wg;
+  k.WPH = p.waves_per_head;
+  k.ngroups = p.head_groups;
+  k.max_pages = a.max_pages;
+  k.R = p.ranges;
+  k.c = a.scale * kLog2e;
+  const __bf16* q = static_cast<const __bf16*>(a.q);
+  const __bf16* kp = static_cast<const __bf16*>(a.k_pool);
+  const __bf16* vp = static_cast<const __bf16*>(a.v_pool);
+  const int32_t* bt = a.block_table;
+  const int32_t* sl = a.seq_lens;
+  int* wsi = static_cast<int*>(a.ws);
+  float* ws_o = static_cast<float*>(a.ws) + p.off_o;
+  float* ws_l = static_cast<float*>(a.ws) + p.off_l;
+  __bf16* o = static_cast<__bf16*>(a.o);
+  float* lse = a.lse;
+  void* fn = select_kernel(a.d, k.G, p.nw);
+  void* args[] = {&k, &q, &kp, &vp, &bt, &sl, &wsi, &ws_o, &ws_l, &o, &lse};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.grid),
+                                 dim3((unsigned)(p.nw * 64)), args, 0,
+                                 a.stream);
+  if (e != hipSuccess) return e;
+  const dim3 mgrid((unsigned)(a.B * a.Hq));
+  if (a.d == 128)
+    hipLaunchKernelGGL((decode_merge_kernel<128>), mgrid, dim3(128), 0,
+                       a.stream, wsi, ws_o, ws_l, sl, a.max_pages, p.ranges,
+                       a.Hq, a.B, o, lse);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<64>), mgrid, dim3(64), 0,
+                       a.stream, wsi, ws_o, ws_l, sl, a.max_pages, p.ranges,
+                       a.Hq, a.B, o, lse);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -35,21 +35,23 @@ struct DecodeArgs {
   float scale;
   void* o;
   float* lse;  // may be null
-  float* ws;   // split partials (null when there is a single split)
-  int pages_per_split, num_splits;
+  void* ws;    // page-range bookkeeping and partials
   hipStream_t stream;
 };
 
-// Split plan shared by the workspace-size query and the launch.
+// Work split shared by the workspace-size query and the launch: the batch's
+// page list is cut into `ranges` equal ranges per KV head; a workgroup of
+// `nw` waves holds `heads_per_wg` KV heads x `waves_per_head` ranges.
 struct DecodePlan {
-  int pages_per_split;
-  int num_splits;
+  int nw, heads_per_wg, waves_per_head, head_groups, ranges;
+  long grid;
+  long off_o, off_l;  // workspace word offsets of partial O and LSE
   size_t workspace_bytes;
 };
 // Returns false when the requested split count cannot be honoured.
 bool plan_decode(int B, int Hq, int Hkv, int d, int max_pages,
                  int num_splits, DecodePlan* plan);
 
-hipError_t launch_paged_decode(const DecodeArgs& a);
+hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan);
 
 }  // namespace fa

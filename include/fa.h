@@ -71,7 +71,7 @@ extern "C" {
 #define FA_ESCALE (-7)          /* softmax scale not finite or not > 0      */
 #define FA_EPAGE (-8)           /* unsupported page size / page count       */
 #define FA_EWORKSPACE (-9)      /* workspace missing or too small           */
-#define FA_ESPLITS (-10)        /* num_splits < 0, or > 256 pages per split */
+#define FA_ESPLITS (-10)        /* num_splits < 0 or > 65536                */
 #define FA_EALIGN (-11)         /* a tensor pointer is not 16-byte aligned
                                    (4-byte for lse, block_table, seq_lens) */
 
@@ -111,10 +111,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * fa_paged_decode_workspace_size - bytes of device workspace that
- * fa_paged_decode needs for these arguments (0 when it needs none).
+ * fa_paged_decode needs for these arguments (always > 0 for valid ones).
  * num_splits: 0 = let the library choose (the same choice fa_paged_decode
- * makes for the same arguments), else the number of KV splits per
- * request. Returns 0 for arguments fa_paged_decode would reject.
+ * makes for the same arguments on the same current device), else the
+ * number of page ranges (see fa_paged_decode). The size grows linearly with
+ * B + ranges. Returns 0 for arguments fa_paged_decode would reject.
  */
 size_t fa_paged_decode_workspace_size(int B, int Hq, int Hkv, int d,
                                       int max_pages_per_seq, int page_size,
@@ -128,11 +129,14 @@ size_t fa_paged_decode_workspace_size(int B, int Hq, int Hkv, int d,
  * For request b with L = seq_lens[b] cached tokens, logical page p holds
  * tokens p*page_size .. p*page_size+page_size-1 in physical page
  * block_table[b, p]. The query attends to all L tokens (no mask inside the
- * context; slots of the last page at or past L are ignored). Each request's
- * pages are split into chunks processed by separate workgroups; every
- * chunk yields a normalised partial output and its LSE, merged with the
- * log-sum-exp form of the two-block merge identity ([Capstone §2.2 step 4],
- * appendix A Q1).
+ * context; slots of the last page at or past L are ignored).
+ *
+ * Split-KV: the pages of all requests, in request order, are cut into R
+ * ranges of equal page count, and each (range, KV head) is processed by
+ * one wave. A request that lies inside one range gets its output from that
+ * wave directly; a request cut by range borders gets a normalised partial
+ * output and its LSE from each range, merged with the log-sum-exp form of
+ * the two-block merge identity ([Capstone §2.2 step 4], appendix A Q1).
  *
  * q            [B, Hq, d] bf16 (one token per request)
  * k_pool,
@@ -146,20 +150,23 @@ size_t fa_paged_decode_workspace_size(int B, int Hq, int Hkv, int d,
  *              dereferenced: that request's O and LSE become NaN.
  * page_size    16.
  * num_pages    number of pages in each pool (for the bounds check above).
- * Hq % Hkv == 0 and Hq / Hkv <= 16.
+ * Hq % Hkv == 0 and Hq / Hkv <= 16; B * max_pages_per_seq <= 2^31 - 1.
  * scale        finite and > 0.
  * o            [B, Hq, d] bf16; lse [B, Hq] fp32 or NULL.
  * workspace    device memory of at least
  *              fa_paged_decode_workspace_size(B, Hq, Hkv, d,
  *              max_pages_per_seq, page_size, num_splits) bytes, 256-byte
- *              aligned; may be NULL when that size is 0. Its contents on
- *              entry do not matter. Two calls that run concurrently must
- *              not share a workspace.
+ *              aligned. Its contents on entry do not matter. Two calls that
+ *              run concurrently must not share a workspace.
  * workspace_bytes  the true size of the buffer `workspace` points to. The
  *              library checks it against the size it needs and cannot check
  *              it against the allocation: a value larger than the buffer
  *              lets the kernels write past its end.
- * num_splits   0 = auto, else the number of chunks per request.
+ * num_splits   0 = auto (about one wave per (range, KV head) for every
+ *              wave the GPU holds at once), else R, the number of page
+ *              ranges, 1..65536 (rounded up to a multiple of the ranges one
+ *              workgroup holds). Any R gives the same result up to fp32
+ *              rounding.
  * stream       hipStream_t or NULL.
  */
 int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,

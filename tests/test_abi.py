@@ -128,7 +128,8 @@ def dec(**kw):
     (dict(page_size=32), L.FA_EPAGE),
     (dict(num_pages=0), L.FA_EPAGE),
     (dict(num_splits=-1), L.FA_ESPLITS),
-    (dict(num_splits=1), L.FA_ESPLITS),              # 512 pages in one split
+    (dict(num_splits=65537), L.FA_ESPLITS),          # above the range cap
+    (dict(B=1 << 22, Hq=8, Hkv=8), L.FA_EINVAL_DIM),  # B * max_pages > 2^31 - 1
     (dict(scale=0.0), L.FA_ESCALE),
     (dict(workspace=None), L.FA_EWORKSPACE),
     (dict(workspace_bytes=16), L.FA_EWORKSPACE),
@@ -140,17 +141,32 @@ def test_decode_rejects(lib, kw, code):
     assert dec(**kw) == code
 
 
+def _ws_bytes(B, Hq, Hkv, d, R):
+    """Workspace of the decode plan, from its documented layout: 64 header
+    words and two per-request ints, rounded up to 64 words; then the partial
+    outputs (B + R) * Hq * d fp32 and their (B + R) * Hq log-sum-exps. R is
+    rounded up to a multiple of the waves per KV head."""
+    G = Hq // Hkv
+    nw = 8 if (Hkv % 8 == 0 and G <= 8) else 4
+    hh = max((c for c in range(1, nw + 1) if Hkv % c == 0),
+             key=lambda c: (c * (nw // c), c))
+    wph = nw // hh
+    R = -(-R // wph) * wph
+    off_o = -(-(64 + 2 * B) // 64) * 64
+    return 4 * (off_o + (B + R) * Hq * d + (B + R) * Hq)
+
+
 def test_workspace_size(lib):
     ws = fa.fa_paged_decode_workspace_size
-    # auto plan for the 64-request, 8-KV-head, 512-page case: 16 splits
-    n = ws(64, 32, 8, 128, 512, 16, 0)
-    assert n == 64 * 32 * 16 * 129 * 4
-    # explicit split counts
-    assert ws(2, 4, 1, 64, 10, 16, 2) == 2 * 4 * 2 * 65 * 4
-    assert ws(2, 4, 1, 64, 10, 16, 1) == 0            # one split: no workspace
-    assert ws(2, 4, 1, 64, 10, 16, 3) == 2 * 4 * 3 * 65 * 4  # 4 pages/split
-    assert ws(2, 4, 1, 64, 10, 16, 4) == 2 * 4 * 4 * 65 * 4  # 3 pages/split -> 4 splits
+    # explicit range counts (one KV head: four ranges per workgroup)
+    assert ws(2, 4, 1, 64, 10, 16, 1) == _ws_bytes(2, 4, 1, 64, 1)
+    assert ws(2, 4, 1, 64, 10, 16, 3) == _ws_bytes(2, 4, 1, 64, 4)
+    assert ws(2, 4, 1, 64, 10, 16, 8) == _ws_bytes(2, 4, 1, 64, 8)
+    assert ws(64, 32, 8, 128, 512, 16, 512) == _ws_bytes(64, 32, 8, 128, 512)
+    assert ws(3, 6, 2, 128, 7, 16, 5) == _ws_bytes(3, 6, 2, 128, 6)
+    # auto: some positive size, at least that of one range
+    assert ws(64, 32, 8, 128, 512, 16, 0) >= _ws_bytes(64, 32, 8, 128, 1)
     # rejected arguments report 0
     assert ws(0, 4, 1, 64, 10, 16, 0) == 0
     assert ws(1, 4, 1, 64, 10, 8, 0) == 0
-    assert ws(1, 4, 1, 64, 600, 16, 1) == 0           # > 256 pages per split
+    assert ws(1, 4, 1, 64, 10, 16, 70000) == 0        # above the range cap

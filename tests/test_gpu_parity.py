@@ -196,15 +196,19 @@ def _gpu_decode(fa, di, num_splits=0, num_pages=None):
     B, Hq, d = q.shape
     npg, page, Hkv, _ = kp.shape
     maxp = bt.shape[1]
-    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    # outputs start as NaN and the workspace as all-ones bytes (NaN floats,
+    # -1 ints), so an output never written or a partial never produced
+    # shows up in the comparison
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16,
+                     device=dev)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev)
     need = fa.fa_paged_decode_workspace_size(B, Hq, Hkv, d, maxp, page,
                                              num_splits)
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    assert need > 0
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=dev)
     fa.fa_paged_decode(q, kp, vp, bt, sl, page,
                        npg if num_pages is None else num_pages, B, Hq, Hkv, d,
-                       maxp, di.scale, out, lse, ws if need else None, need,
-                       num_splits)
+                       maxp, di.scale, out, lse, ws, ws.numel(), num_splits)
     torch.cuda.synchronize()
     return out.double().cpu().numpy(), lse.double().cpu().numpy()
 
@@ -235,6 +239,49 @@ def test_decode_many_splits_and_long(fa):
         o, lse = _gpu_decode(fa, di, ns)
         ro, rl = _oracle_decode(di)
         _compare(o, lse, ro, rl, "bf16", f"long decode splits={ns}")
+
+
+def test_decode_empty_requests_and_empty_ranges(fa):
+    # empty requests first, last and in between; more ranges than pages, so
+    # some ranges are empty and requests span runs of one-page ranges
+    lens = [0, 0, 300, 0, 1, 17, 0, 0]
+    di = W.decode_inputs(len(lens), 16, 4, 128, lens=lens, max_pages=20,
+                         seed=11)
+    ro, rl = _oracle_decode(di)
+    for ns in (1, 2, 5, 23, 64, 1000):
+        o, lse = _gpu_decode(fa, di, ns)
+        _compare(o, lse, ro, rl, "bf16", f"sparse decode splits={ns}")
+        assert np.all(o[[0, 1, 3, 6, 7]] == 0)
+        assert np.all(np.isneginf(lse[[0, 1, 3, 6, 7]]))
+
+
+def test_decode_workspace_reuse(fa):
+    # the workspace of one call, reused as is by a call with another batch
+    # and range count: nothing of the first call may leak into the second
+    dev = torch.device("cuda:0")
+    a = W.decode_inputs(5, 8, 2, 64, lens=[700, 3, 0, 2000, 64],
+                        max_pages=128, seed=21)
+    b = W.decode_inputs(4, 8, 2, 64, lens=[1, 0, 1500, 20], max_pages=128,
+                        seed=22)
+    sizes = [fa.fa_paged_decode_workspace_size(5, 8, 2, 64, 128, 16, ns)
+             for ns in (64, 7)]
+    ws = torch.full((max(sizes),), 255, dtype=torch.uint8, device=dev)
+    outs = []
+    for di, ns in ((a, 64), (b, 7)):
+        q = di.q.to(dev)
+        kp, vp = di.k_pool.to(dev), di.v_pool.to(dev)
+        bt, sl = di.block_table.to(dev), di.seq_lens.to(dev)
+        B, Hq, d = q.shape
+        o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16,
+                       device=dev)
+        lse = torch.full((B, Hq), float("nan"), device=dev)
+        fa.fa_paged_decode(q, kp, vp, bt, sl, 16, kp.shape[0], B, Hq, 2, d,
+                           128, di.scale, o, lse, ws, ws.numel(), ns)
+        torch.cuda.synchronize()
+        outs.append((o.double().cpu().numpy(), lse.double().cpu().numpy()))
+    for (o, lse), di, tag in zip(outs, (a, b), ("first", "second")):
+        ro, rl = _oracle_decode(di)
+        _compare(o, lse, ro, rl, "bf16", f"workspace reuse, {tag} call")
 
 
 def test_decode_bad_page_id_gives_nan(fa):
