@@ -15,6 +15,8 @@
 //   -> per wave: S^T = K Q^T (Q lives in VGPRs for the whole tile),
 //      online softmax, P^T packed to bf16 in registers, O^T += V^T P^T with
 //      the V^T operand produced by gfx950's LDS transpose read.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -69,9 +71,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,
     float c) {
   using T = Lay<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::K_BYTES + 2 * T::V_BYTES];
-  lds_char* const kbuf0 = (lds_char*)smem;
-  lds_char* const vbuf0 = kbuf0 + 2 * T::K_BYTES;
+  // Four separate arrays, always selected by a compile-time index: the
+  // compiler can then tell that reading one buffer does not depend on the
+  // direct loads still in flight into another, and waits only where a
+  // buffer is actually reused.
+  __shared__ __attribute__((aligned(16))) char k_lds0[T::K_BYTES];
+  __shared__ __attribute__((aligned(16))) char k_lds1[T::K_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds0[T::V_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds1[T::V_BYTES];
+  auto kbuf = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)k_lds0;
+    else return (lds_char*)k_lds1;
+  };
+  auto vbuf = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)v_lds0;
+    else return (lds_char*)v_lds1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,10 +139,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     koff[i] = k_row(w + 4 * i) * D + 8 * chunk;
     voff[i] = v_row(w + 4 * i) * D + 8 * chunk;
   }
-  auto issue_k = [&](int tile, int buf) {
+  auto issue_k = [&](int tile, auto buf) {
     const int n0 = tile * kBN;
     const __bf16* src = Kh + (long)n0 * D;
-    lds_char* dst = kbuf0 + buf * T::K_BYTES + w * T::KPITCH;
+    lds_char* dst = kbuf(buf) + w * T::KPITCH;
     if (n0 + kBN <= Nk) {
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
@@ -140,10 +155,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                   dst + 4 * i * T::KPITCH);
     }
   };
-  auto issue_v = [&](int tile, int buf) {
+  auto issue_v = [&](int tile, auto buf) {
     const int n0 = tile * kBN;
     const __bf16* src = Vh + (long)n0 * D;
-    lds_char* dst = vbuf0 + buf * T::V_BYTES + w * T::VPITCH;
+    lds_char* dst = vbuf(buf) + w * T::VPITCH;
     if (n0 + kBN <= Nk) {
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
@@ -164,8 +179,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                     (16 * ((lane >> 4) & 1) + 4 * (i16 & 3)) * 2;
   // S^T = K Q^T for the two 32-key blocks of a tile (two independent
   // accumulation chains, interleaved)
-  auto qk = [&](int buf, f32x16 (&s)[2]) {
-    const lds_char* kp = kbuf0 + buf * T::K_BYTES + kfrag;
+  auto qk = [&](auto buf, f32x16 (&s)[2]) {
+    const lds_char* kp = kbuf(buf) + kfrag;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -184,26 +199,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
 
   // ---- prologue: K(0), V(0), K(1) in flight; S(0)
+  constexpr std::integral_constant<int, 0> B0{};
+  constexpr std::integral_constant<int, 1> B1{};
   if (nt > 0) {
-    issue_k(0, 0);
-    issue_v(0, 0);
-    if (nt > 1) issue_k(1, 1);
+    issue_k(0, B0);
+    issue_v(0, B0);
+    if (nt > 1) issue_k(1, B1);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 sc[2];
-  if (nt > 0 && !skip_tile(0)) qk(0, sc);
+  if (nt > 0 && !skip_tile(0)) qk(B0, sc);
   __syncthreads();  // K buffer 0 is refilled below
 
-  for (int t = 0; t < nt; ++t) {
+  // One key tile: S(t) arrives in sc; S(t+1) is computed into sn while P(t)
+  // is formed. Tiles are taken in pairs with the two score buffers swapping
+  // roles, so no tile ends with a register copy.
+  // `par` is t % 2 as a compile-time index.
+  auto step = [&](int t, auto par, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr int P = decltype(par)::value;
+    constexpr std::integral_constant<int, P> cur{};
+    constexpr std::integral_constant<int, 1 - P> nxt{};
     const int n0 = t * kBN;
     // K runs two tiles ahead, V one: both target buffers were last read
     // before the previous barrier.
-    if (t + 2 < nt) issue_k(t + 2, t & 1);
-    if (t + 1 < nt) issue_v(t + 1, (t + 1) & 1);
+    if (t + 2 < nt) issue_k(t + 2, cur);
+    if (t + 1 < nt) issue_v(t + 1, nxt);
     const bool do_t = !skip_tile(t);
-    const bool do_n = (t + 1 < nt) && !skip_tile(t + 1);
-    f32x16 sn[2];
     if (do_t) {
       // mask the ragged end of the key range and the causal diagonal
       const bool need_mask =
@@ -219,23 +241,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           }
       }
       const float alpha = softmax_reference<2>(sc, st, c);
-      uint32_t pw[2][2][4];
-      // S(t+1) on the matrix cores while P(t) is formed on the VALU
-      if (do_n) {
-        qk((t + 1) & 1, sn);
-        softmax_exp_pack<2>(sc, st, c, pw);
-      } else {
-        softmax_exp_pack<2>(sc, st, c, pw);
-      }
+      // rescale O before the MFMA work below, so that the S(t+1) product
+      // and the P(t) arithmetic share one branch-free block
       if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) o[mb][v] *= alpha;
       }
+      uint32_t pw[2][2][4];
+      // S(t+1) on the matrix cores while P(t) is formed on the VALU. Run
+      // without a branch (so both sit in one basic block and interleave):
+      // past the last tile, or beyond this wave's causal rows, the result is
+      // never read, and the K buffer it reads is not being written.
+      qk(nxt, sn);
+      softmax_exp_pack<2>(sc, st, c, pw);
       // O^T += V^T P^T, 16 keys per MFMA: lane half h contracts keys
       // 32kb + 16j + 4h + {0..3} (items 0..3) and +8 (items 4..7)
-      const lds_char* vp0 = vbuf0 + (t & 1) * T::V_BYTES + vfrag;
+      const lds_char* vp0 = vbuf(cur) + vfrag;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -257,12 +280,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           }
         }
     }
-    if (do_n) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sc[kb] = sn[kb];
-    }
     wait_vm0();
     __syncthreads();
+  };
+  f32x16 sb[2];
+  for (int t = 0; t < nt; t += 2) {
+    step(t, B0, sc, sb);
+    if (t + 1 < nt) step(t + 1, B1, sb, sc);
   }
 
   // ---- epilogue: O = O^T / lr, LSE = ln 2 * (m + log2 l)
