@@ -349,58 +349,75 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   }
 }
 
-// One workgroup per (request, query head): merge the pieces of requests
-// that a range border cut; write O = 0, LSE = -inf for empty requests.
+// One wave per (request, query head): merge the pieces of requests that a
+// range border cut; write O = 0, LSE = -inf for empty requests. A lane owns
+// D/64 output columns. The bookkeeping words are read together, then the
+// pieces are taken four at a time with all their loads issued before any
+// is used (one online merge over the pieces), so the kernel waits for few
+// memory round trips.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(
+__global__ __launch_bounds__(64) void decode_merge_kernel(
     const int* __restrict__ wsi, const float* __restrict__ ws_o,
     const float* __restrict__ ws_l, const int32_t* __restrict__ SL,
     int max_pages, int R, int Hq, int B, __bf16* __restrict__ O,
     float* __restrict__ LSE) {
-  const int hq = blockIdx.x;  // b * Hq + h
-  const int b = hq / Hq;
-  const int d = threadIdx.x;
-  const int npg = pages_of(SL[b], max_pages * kPage);
-  if (npg == 0) {
-    O[(long)hq * D + d] = (__bf16)0.f;
-    if (d == 0 && LSE != nullptr) LSE[hq] = kNegInf;
-    return;
-  }
+  constexpr int DPL = D / 64;
+  const long hq = blockIdx.x;  // b * Hq + h
+  const int b = (int)(hq / Hq);
+  const int h = (int)(hq - (long)b * Hq);
+  const int lane = threadIdx.x;
+  const int len = SL[b];
   const int r_first = wsi[kFirstWord + b];
   const int r_last = wsi[kFirstWord + B + b];
-  if (r_first == r_last) return;  // one piece: written as the final output
   const long T = wsi[0];
+  __bf16* orow = O + hq * D + DPL * lane;
+  if (pages_of(len, max_pages * kPage) == 0) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) orow[e] = (__bf16)0.f;
+    if (lane == 0 && LSE != nullptr) LSE[hq] = kNegInf;
+    return;
+  }
+  if (r_first == r_last) return;  // one piece: written as the final output
   // ranges strictly inside [r_first, r_last] may be empty (T < R)
   auto live = [&](int r) {
-    return (long)r * T / R < (long)(r + 1) * T / R;
+    return r <= r_last && (long)r * T / R < (long)(r + 1) * T / R;
   };
-  float M = kNegInf;
+  float M = kNegInf, tot = 0.f, acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
   bool nan = false;
-  for (int r = r_first; r <= r_last; ++r) {
-    if (!live(r)) continue;
-    const float x = ws_l[((long)b + r) * Hq + (hq - (long)b * Hq)];
-    nan |= (x != x);
-    M = fmaxf(M, x);
-  }
-  float od = 0.f, L_out = kNegInf;
-  if (M != kNegInf) {
-    float tot = 0.f, acc = 0.f;
-    for (int r = r_first; r <= r_last; ++r) {
-      if (!live(r)) continue;
-      const long ph = ((long)b + r) * Hq + (hq - (long)b * Hq);
-      const float f = fast_exp2((ws_l[ph] - M) * kLog2e);
-      tot += f;
-      acc += f * ws_o[ph * D + d];
+  for (int r0 = r_first; r0 <= r_last; r0 += 4) {
+    float lj[4], oj[4][DPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = live(r0 + u);
+      const long ph = ((long)b + (ok ? r0 + u : r_first)) * Hq + h;
+      lj[u] = ok ? ws_l[ph] : kNegInf;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) oj[u][e] = ok ? ws_o[ph * D + DPL * lane + e] : 0.f;
     }
-    od = acc / tot;
-    L_out = M + fast_log2(tot) * kLn2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      nan |= (lj[u] != lj[u]);
+      if (!(lj[u] > kNegInf)) continue;  // empty range or NaN: weight 0
+      const float mn = fmaxf(M, lj[u]);
+      const float fo = (M == kNegInf) ? 0.f : fast_exp2((M - mn) * kLog2e);
+      const float fj = fast_exp2((lj[u] - mn) * kLog2e);
+      tot = tot * fo + fj;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = acc[e] * fo + fj * oj[u][e];
+      M = mn;
+    }
   }
+  float inv = M != kNegInf ? 1.f / tot : 0.f;
+  float L_out = M != kNegInf ? M + fast_log2(tot) * kLn2 : kNegInf;
   if (nan) {
-    od = __builtin_nanf("");
+    inv = __builtin_nanf("");
     L_out = __builtin_nanf("");
   }
-  O[(long)hq * D + d] = (__bf16)od;
-  if (d == 0 && LSE != nullptr) LSE[hq] = L_out;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) orow[e] = (__bf16)(acc[e] * inv);
+  if (lane == 0 && LSE != nullptr) LSE[hq] = L_out;
 }
 
 template <int D, int GP, int NW>
@@ -505,7 +522,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p) {
   if (e != hipSuccess) return e;
   const dim3 mgrid((unsigned)(a.B * a.Hq));
   if (a.d == 128)
-    hipLaunchKernelGGL((decode_merge_kernel<128>), mgrid, dim3(128), 0,
+    hipLaunchKernelGGL((decode_merge_kernel<128>), mgrid, dim3(64), 0,
                        a.stream, wsi, ws_o, ws_l, sl, a.max_pages, p.ranges,
                        a.Hq, a.B, o, lse);
   else
