@@ -263,7 +263,7 @@ def main():
         gbs = info["decode"]["bytes"] / t / 1e9
         out["decode"] = {
             "value": gbs, "unit": "GB/s", "frac_hbm_peak": gbs / PEAK_HBM_GBS,
-            "roofline": {"kernel": "decode_split_kernel + decode_merge_kernel",
+            "roofline": {"kernel": "decode_kernel + decode_merge_kernel",
                          "bound": "hbm", "achieved": gbs,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS,
