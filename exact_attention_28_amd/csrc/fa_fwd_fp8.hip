@@ -10,11 +10,17 @@
 // e4m3 without a scale. O is normalised by the sum of the rounded P (an
 // exact convex combination of V rows), LSE uses the sum of the fp32 P.
 //
-// Structure as the bf16 kernel (128-row Q tile, 64-key K/V tiles,
-// double-buffered swizzled LDS, S^T / O^T register layout) on
-// v_mfma_f32_32x32x64_f8f6f4: one MFMA contracts 64 elements, so Q K^T
-// takes D/64 steps per 32-key block and one P V step covers the whole
-// 64-key tile.
+// Structure as the bf16 kernel: one workgroup (4 waves, 32 rows each) per
+// 128-row query tile, 64-key K/V tiles arriving by direct global->LDS loads
+// into a double-buffered LDS stage, S^T / O^T register layout, tiles taken
+// in pairs so that S(t+1) is computed while P(t) is formed. The products
+// run on v_mfma_f32_32x32x64_f8f6f4: Q K^T takes D/64 steps per 32-key
+// block, and one P V step covers the whole 64-key tile. The V^T operand
+// comes from gfx950's 8-bit LDS transpose read. The sum of the rounded P
+// comes from one more MFMA per tile against an all-ones operand: every
+// output row of ones . P^T is the row sum of P, accumulated exactly.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -25,29 +31,57 @@ constexpr int kBM = 128;
 constexpr int kBN = 64;
 constexpr int kThreads = 256;
 
+// ------------------------------------------------------------ LDS layout
+// A tile is 64 rows of D bytes, stored as 1 KB blocks (one direct load
+// instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B, so the 16-byte
+// units of equal block-relative offset rotate through the eight 16-byte
+// bank groups from block to block.
+//  * K: block b holds rows b, b + NB, b + 2NB, ... The S^T = K Q^T A
+//    operand (32 bytes per lane: key 32kb + r32, bytes 64sd + 32h ..) is
+//    read as two 16-byte reads; the eight lanes served together hold eight
+//    consecutive keys, which sit in different blocks (D = 128) or in the
+//    same slot of four blocks and the next slot (D = 64): conflict free.
+//  * V: read with ds_read_b64_tr_b8, which in each 16-lane group takes
+//    eight rows of 16 bytes (lane j names half j%2 of row j/2) and hands
+//    lane i byte i of every row. One read gives a lane 8 keys of its d
+//    column; the 8 keys of a read are k0..k0+3 and k0+8..k0+11 (the S^T
+//    accumulator order), and the layout puts them in eight different bank
+//    groups:
+//      D = 128: block (r%4) + 4((r/8)%2), slot (r/4)%2 + 2(r/16)
+//      D = 64:  block r%4, slot 8((r/4)%2) + r/8
 template <int D>
-struct Fp8Tile {
-  static constexpr int CPR = D / 16;                    // 16 B chunks / K row
-  static constexpr int K_BYTES = kBN * D;
-  static constexpr int VT_ROW = kBN;                    // 64 keys, 4 chunks
-  static constexpr int VT_BYTES = D * VT_ROW;
-  static constexpr int STAGE = K_BYTES + VT_BYTES;
-  static constexpr int KLOADS = kBN * CPR / kThreads;   // 2 (D=128), 1 (D=64)
-  static constexpr int VUNITS = (kBN / 4) * (D / 8);    // 4 keys x 8 d
+struct Lay8 {
+  static constexpr int RPB = 1024 / D;   // rows per 1 KB block
+  static constexpr int NB = kBN / RPB;   // blocks per tile
+  static constexpr int CPR = D / 16;     // 16-byte chunks per row
+  static constexpr int PITCH = 1040;
+  static constexpr int BYTES = NB * PITCH;
+  static constexpr int BPW = NB / 4;     // blocks each wave loads
 };
-
 template <int D>
-__device__ __forceinline__ int k_chunk(int key, int c) {
-  if constexpr (D == 128) return c ^ ((key >> 1) & 7);   // 2 rows / 256 B
-  else return c ^ ((key >> 2) & 3);                      // 4 rows / 256 B
+__device__ __forceinline__ int v_block(int r) {
+  if constexpr (D == 128) return (r & 3) + 4 * ((r >> 3) & 1);
+  else return r & 3;
 }
-__device__ __forceinline__ int vt_chunk(int d, int c) {
-  return c ^ ((d >> 2) & 3);  // 4 V^T rows per 256 B
+template <int D>
+__device__ __forceinline__ int v_slot(int r) {
+  if constexpr (D == 128) return ((r >> 2) & 1) + 2 * (r >> 4);
+  else return 8 * ((r >> 2) & 1) + (r >> 3);
 }
-// Position of key k of the tile inside a V^T row: with k = 32*kb + 8*g +
-// 4*h + r, pos = 32*h + 16*kb + 4*g + r, so MFMA lane half h reads its 32
-// keys as one contiguous 32 B run in the order of the S^T accumulator
-// elements (block kb, element 4g + r).
+// inverse: the row stored at (block, slot)
+template <int D>
+__device__ __forceinline__ int v_row(int b, int s) {
+  if constexpr (D == 128) return 16 * (s >> 1) + 8 * (b >> 2) + 4 * (s & 1) + (b & 3);
+  else return 8 * (s & 7) + 4 * (s >> 3) + b;
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
+                                   16, 0, 0);
+}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
@@ -55,8 +89,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk, float c,
     float s_v) {
-  using T = Fp8Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  using T = Lay8<D>;
+  __shared__ __attribute__((aligned(16))) char k_lds0[T::BYTES];
+  __shared__ __attribute__((aligned(16))) char k_lds1[T::BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds0[T::BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds1[T::BYTES];
+  auto kbuf = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)k_lds0;
+    else return (lds_char*)k_lds1;
+  };
+  auto vbuf = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)v_lds0;
+    else return (lds_char*)v_lds1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -69,7 +114,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const int hk = ti.hq / (Hq / Hkv);
   const int q0 = ti.qt * kBM;
   const long qbase = (long)(ti.b * Hq + ti.hq) * Nq * D;
-  const long kvbase = (long)(ti.b * Hkv + hk) * Nk * D;
+  const uint8_t* Kh = K + (long)(ti.b * Hkv + hk) * Nk * D;
+  const uint8_t* Vh = V + (long)(ti.b * Hkv + hk) * Nk * D;
   const int off = Nk - Nq;
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, min(q0 + kBM, Nq) + off);
@@ -78,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const int wrow0 = q0 + w * 32;
   const int row = wrow0 + r32;
   const int rowc = min(row, Nq - 1);
-  // Q fragments: row r32, d = 64*s + 32*h + t (t = 0..31)
+  // Q fragments (B operand of S^T = K Q^T): row r32, d = 64*s + 32*h + t
   i32x8 qf[D / 64];
 #pragma unroll
   for (int s = 0; s < D / 64; ++s) {
@@ -94,95 +140,109 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
+  // row sums of the rounded P (every element holds this lane's row sum;
+  // only element 0 is kept up to date under rescaling)
+  f32x16 lsum;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) lsum[v] = 0.f;
   RowState st{kNegInf, 0.f, 0.f};
+  // e4m3 1.0 in every byte
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
 
-  u32x4 kr[T::KLOADS];
-  u32x2 vr[4];
-  constexpr int VDC = D / 8;
-  const int vkg = tid / VDC, vdc = tid % VDC;
-  auto load_tile = [&](int n0) {
+  // ---- direct loads. Wave w fills blocks w, w+4, ...; lane l moves chunk
+  // l % CPR of the block's slot l / CPR. On the ragged last tile rows past
+  // Nk are clamped to the last key (their scores are masked, P is 0).
+  const int slot = lane / T::CPR, chunk = lane % T::CPR;
+  auto k_row = [&](int b) { return b + T::NB * slot; };
+  auto issue_k = [&](int tile, auto buf) {
+    const int n0 = tile * kBN;
+    const uint8_t* src = Kh + (long)n0 * D + 16 * chunk;
+    lds_char* dst = kbuf(buf) + w * T::PITCH;
+    const int last = min(kBN, Nk - n0) - 1;
 #pragma unroll
-    for (int i = 0; i < T::KLOADS; ++i) {
-      const int u = tid + kThreads * i;
-      const int key = u / T::CPR, cc = u % T::CPR;
-      const int gk = n0 + key;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kr[i] = gk < Nk ? *reinterpret_cast<const u32x4*>(K + kvbase +
-                                                        (long)gk * D + 16 * cc)
-                      : z;
-    }
-    if (tid < T::VUNITS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gk = n0 + 4 * vkg + r;
-        u32x2 z = {0u, 0u};
-        vr[r] = gk < Nk ? *reinterpret_cast<const u32x2*>(
-                              V + kvbase + (long)gk * D + 8 * vdc)
-                        : z;
-      }
-    }
+    for (int i = 0; i < T::BPW; ++i)
+      g2lds_16B(src + (long)min(k_row(w + 4 * i), last) * D,
+                dst + 4 * i * T::PITCH);
   };
-  auto store_tile = [&](int stage) {
-    char* ks = smem + stage * T::STAGE;
-    char* vs = ks + T::K_BYTES;
+  auto issue_v = [&](int tile, auto buf) {
+    const int n0 = tile * kBN;
+    const uint8_t* src = Vh + (long)n0 * D + 16 * chunk;
+    lds_char* dst = vbuf(buf) + w * T::PITCH;
+    const int last = min(kBN, Nk - n0) - 1;
 #pragma unroll
-    for (int i = 0; i < T::KLOADS; ++i) {
-      const int u = tid + kThreads * i;
-      const int key = u / T::CPR, cc = u % T::CPR;
-      *reinterpret_cast<u32x4*>(ks + key * D + k_chunk<D>(key, cc) * 16) = kr[i];
-    }
-    if (tid < T::VUNITS) {
-      const int cpos = 2 * (vkg & 1) + (vkg >> 3);
-      const int dw = (vkg >> 1) & 3;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * vdc + e;
-        const int b = e & 3;
-        const uint32_t w0 = vr[0][e >> 2], w1 = vr[1][e >> 2];
-        const uint32_t w2 = vr[2][e >> 2], w3 = vr[3][e >> 2];
-        // byte b of keys 0..3 -> bytes 0..3 of one word
-        const uint32_t sel = (uint32_t)b | ((uint32_t)(b + 4) << 8);
-        const uint32_t lo = __builtin_amdgcn_perm(w1, w0, sel);   // k0, k1
-        const uint32_t hi = __builtin_amdgcn_perm(w3, w2, sel);   // k2, k3
-        const uint32_t word = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vs + d * T::VT_ROW +
-                                     vt_chunk(d, cpos) * 16 + dw * 4) = word;
-      }
-    }
+    for (int i = 0; i < T::BPW; ++i)
+      g2lds_16B(src + (long)min(v_row<D>(w + 4 * i, slot), last) * D,
+                dst + 4 * i * T::PITCH);
   };
 
-  if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < nt; ++t) {
-    const int n0 = t * kBN;
-    const bool has_next = t + 1 < nt;
-    if (has_next) load_tile(n0 + kBN);
-    const bool skip = CAUSAL && (n0 > wrow0 + 31 + off);
-    if (!skip) {
-      const char* ks = smem + (t & 1) * T::STAGE;
-      const char* vs = ks + T::K_BYTES;
-      f32x16 s[2];
+  // ---- per-lane fragment bases
+  // K: row 32kb + r32 is in block r32 % NB (NB divides 32), slot
+  // (32kb + r32) / NB; bytes 64sd + 32h (+16).
+  const int kfrag = (r32 % T::NB) * T::PITCH + (r32 / T::NB) * D + 32 * h;
+  auto qk = [&](auto buf, f32x16 (&s)[2]) {
+    const lds_char* kp = kbuf(buf) + kfrag;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+    for (int sd = 0; sd < D / 64; ++sd)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-        const int key = 32 * kb + r32;
-#pragma unroll
-        for (int sd = 0; sd < D / 64; ++sd) {
-          const int c0 = 4 * sd + 2 * h;
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(
-              ks + key * D + k_chunk<D>(key, c0) * 16);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(
-              ks + key * D + k_chunk<D>(key, c0 + 1) * 16);
-          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          s[kb] = mfma_32x32x64_e4m3(a, qf[sd], s[kb]);
-        }
+        const lds_char* p = kp + kb * (32 / T::NB) * D + 64 * sd;
+        const u32x4 a0 = *(const __attribute__((address_space(3))) u32x4*)(p);
+        const u32x4 a1 = *(const __attribute__((address_space(3))) u32x4*)(p + 16);
+        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        s[kb] = mfma_32x32x64_e4m3(a, qf[sd], s[kb]);
       }
+  };
+  // V^T: lane (r32, h) needs, for d = 32mb + r32, the keys of P's byte
+  // order: byte t of 32 = key 32(t/16) + 8((t%16)/4) + 4h + t%4. Read j
+  // (t = 8j..8j+7): this lane names row u = (r32%16)/2 of the read, i.e.
+  // key 32(j/2) + 16(j%2) + 8(u/4) + 4h + u%4, bytes 16(r32/16) + 8(r32%2)
+  // of the 32-column block mb.
+  int vaddr[4];
+  {
+    const int u = (r32 & 15) >> 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = 32 * (j >> 1) + 16 * (j & 1) + 8 * (u >> 2) + 4 * h + (u & 3);
+      vaddr[j] = v_block<D>(key) * T::PITCH + v_slot<D>(key) * D +
+                 16 * (r32 >> 4) + 8 * (r32 & 1);
+    }
+  }
+  auto skip_tile = [&](int tile) {
+    return CAUSAL && (tile * kBN > wrow0 + 31 + off);
+  };
+
+  // ---- prologue: K(0), V(0), K(1) in flight; S(0)
+  constexpr std::integral_constant<int, 0> B0{};
+  constexpr std::integral_constant<int, 1> B1{};
+  if (nt > 0) {
+    issue_k(0, B0);
+    issue_v(0, B0);
+    if (nt > 1) issue_k(1, B1);
+  }
+  wait_vm0();
+  __syncthreads();
+  f32x16 sc[2];
+  if (nt > 0 && !skip_tile(0)) qk(B0, sc);
+  __syncthreads();  // K buffer 0 is refilled below
+
+  // One key tile t (parity P): S(t) arrives in sc, S(t+1) is computed into
+  // sn while P(t) is formed. K runs two tiles ahead and V one: both target
+  // buffers were last read before the previous barrier. Tiles are taken in
+  // pairs with the score buffers swapping roles (no register copies).
+  auto step = [&](int t, auto par, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr int P = decltype(par)::value;
+    constexpr std::integral_constant<int, P> cur{};
+    constexpr std::integral_constant<int, 1 - P> nxt{};
+    const int n0 = t * kBN;
+    if (t + 2 < nt) issue_k(t + 2, cur);
+    if (t + 1 < nt) issue_v(t + 1, nxt);
+    if (!skip_tile(t)) {
       const bool need_mask =
           (n0 + kBN > Nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
       if (need_mask) {
@@ -192,38 +252,64 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (key > lim) s[kb][v] = kNegInf;
+            if (key > lim) sc[kb][v] = kNegInf;
           }
       }
-      online_softmax_tile<2, D / 32>(s, o, st, c);
-      // P^T as e4m3: byte t = 16*kb + v of this lane's 32 keys
+      const float alpha = softmax_reference<2>(sc, st, c);
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[mb][v] *= alpha;
+        lsum[0] *= alpha;
+      }
+      // S(t+1) on the matrix cores while P(t) is formed on the VALU (past
+      // the last tile, or beyond this wave's causal rows, the product is
+      // never read and its buffer is not being written)
+      qk(nxt, sn);
+      const float mref = (st.m == kNegInf) ? 0.f : st.m;
+      float sum = 0.f;
       i32x8 pb;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kb = j >> 2, v0 = 4 * (j & 3);
-        const uint32_t w8 = pack_e4m3x4(s[kb][v0], s[kb][v0 + 1],
-                                        s[kb][v0 + 2], s[kb][v0 + 3]);
-        st.lr = add_e4m3x4(w8, st.lr);
-        pb[j] = (int)w8;
+      for (int jj = 0; jj < 8; ++jj) {
+        const int kb = jj >> 2, v0 = 4 * (jj & 3);
+        float p4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p4[e] = fast_exp2(__builtin_fmaf(sc[kb][v0 + e], c, -mref));
+          sum += p4[e];
+        }
+        pb[jj] = (int)pack_e4m3x4(p4[0], p4[1], p4[2], p4[3]);
       }
+      st.l += sum;
+      lsum = mfma_32x32x64_e4m3(ones, pb, lsum);
+      const lds_char* vp = vbuf(cur);
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
-        const int dd = 32 * mb + r32;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(
-            vs + dd * T::VT_ROW + vt_chunk(dd, 2 * h) * 16);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(
-            vs + dd * T::VT_ROW + vt_chunk(dd, 2 * h + 1) * 16);
-        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        i32x8 a;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          typedef int v2i __attribute__((ext_vector_type(2)));
+          const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) v2i*)(vp + vaddr[j] + 32 * mb));
+          a[2 * j] = r[0];
+          a[2 * j + 1] = r[1];
+        }
         o[mb] = mfma_32x32x64_e4m3(a, pb, o[mb]);
       }
     }
-    if (has_next) store_tile((t + 1) & 1);
+    wait_vm0();
     __syncthreads();
+  };
+  f32x16 sb[2];
+  for (int t = 0; t < nt; t += 2) {
+    step(t, B0, sc, sb);
+    if (t + 1 < nt) step(t + 1, B1, sb, sc);
   }
 
-  const float ltot = st.l + xor_lane(st.l, 32);
-  const float lrtot = st.lr + xor_lane(st.lr, 32);
+  // ---- epilogue: O = s_v * O^T / lr, LSE = ln 2 * (m + log2 l)
+  const float ltot = sum_halves(st.l);
+  const float lrtot = lsum[0];
   if (row < Nq) {
     const bool live = ltot > 0.f;
     const float inv = live ? s_v / lrtot : 0.f;
