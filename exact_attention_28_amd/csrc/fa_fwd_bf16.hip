@@ -26,6 +26,7 @@ namespace {
 constexpr int kBM = 128;       // query rows per workgroup (32 per wave)
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;  // 4 waves
+constexpr int kWaves = kThreads / 64;
 
 // ------------------------------------------------------------ LDS layout
 // K and V tiles (64 rows x d) arrive by direct global->LDS loads
@@ -52,7 +53,7 @@ struct Lay {
   static constexpr int VPITCH = D == 128 ? 1040 : 1056;
   static constexpr int K_BYTES = NB * KPITCH;
   static constexpr int V_BYTES = NB * VPITCH;
-  static constexpr int BPW = NB / 4;            // blocks each wave loads
+  static constexpr int BPW = NB / kWaves;       // blocks each wave loads
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -65,7 +66,7 @@ __device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
   RowState st{kNegInf, 0.f, 0.f};
 
-  // ---- direct loads. Wave w fills blocks w, w+4, ...; lane l moves chunk
+  // ---- direct loads. Wave w fills blocks w, w + kWaves, ...; lane l moves chunk
   // l % CPR of the block's slot l / CPR. Full tiles use precomputed lane
   // offsets; on the ragged last tile rows past Nk are clamped to the last
   // key (their scores are masked, their P is 0).
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   int koff[T::BPW], voff[T::BPW];
 #pragma unroll
   for (int i = 0; i < T::BPW; ++i) {
-    koff[i] = k_row(w + 4 * i) * D + 8 * chunk;
-    voff[i] = v_row(w + 4 * i) * D + 8 * chunk;
+    koff[i] = k_row(w + kWaves * i) * D + 8 * chunk;
+    voff[i] = v_row(w + kWaves * i) * D + 8 * chunk;
   }
   auto issue_k = [&](int tile, auto buf) {
     const int n0 = tile * kBN;
@@ -146,13 +147,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     if (n0 + kBN <= Nk) {
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(src + koff[i], dst + 4 * i * T::KPITCH);
+        g2lds_16B(src + koff[i], dst + kWaves * i * T::KPITCH);
     } else {
       const int last = Nk - 1 - n0;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(src + min(k_row(w + 4 * i), last) * D + 8 * chunk,
-                  dst + 4 * i * T::KPITCH);
+        g2lds_16B(src + min(k_row(w + kWaves * i), last) * D + 8 * chunk,
+                  dst + kWaves * i * T::KPITCH);
     }
   };
   auto issue_v = [&](int tile, auto buf) {
@@ -162,13 +163,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     if (n0 + kBN <= Nk) {
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(src + voff[i], dst + 4 * i * T::VPITCH);
+        g2lds_16B(src + voff[i], dst + kWaves * i * T::VPITCH);
     } else {
       const int last = Nk - 1 - n0;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(src + min(v_row(w + 4 * i), last) * D + 8 * chunk,
-                  dst + 4 * i * T::VPITCH);
+        g2lds_16B(src + min(v_row(w + kWaves * i), last) * D + 8 * chunk,
+                  dst + kWaves * i * T::VPITCH);
     }
   };
 
