@@ -1,10 +1,11 @@
-"""fp64 CPU oracle for exact attention and paged decode.
+"""fp64 CPU oracle for exact attention (forward and backward) and paged decode.
 
 Test infrastructure only: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py``, never by the product path.
 """
 from .attention import (  # noqa: F401
     attention,
+    attention_backward,
     attention_fp8,
     gather_paged_kv,
     merge_partials,

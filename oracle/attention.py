@@ -40,6 +40,13 @@ notes of the repository):
   multiplies them out in fp64 (exact) and does NOT model the kernel's
   re-quantisation of P ([FA3-guide] ``flash_attn_v3_fp8`` listing).
 
+Backward: the pages say only that the backward pass re-computes P on chip
+from Q, K and the saved row statistics instead of reading a stored P
+([Capstone §6.1], the row about writing P to HBM; §7.3 question 1). What it
+must produce is the gradient of the definition, which the oracle writes out
+with the chain rule through the materialised softmax (see
+``attention_backward``).
+
 Pins: every function here is checked by ``tests/test_oracle_pins.py``
 against values the pages print, closed forms, invariants and brute force.
 The fp8 path's re-quantisation error of P is the one part left unpinned
@@ -60,6 +67,7 @@ __all__ = [
     "merge_partials",
     "gather_paged_kv",
     "paged_decode",
+    "attention_backward",
 ]
 
 
@@ -257,3 +265,62 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, page_size, scale):
         out[b] = o[0, :, 0, :]
         lse[b] = s[0, :, 0]
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# Attention backward (the gradient of the definition)
+# --------------------------------------------------------------------------
+def attention_backward(q, k, v, do, scale, causal=False):
+    """Gradients of O = softmax(scale * Q K^T) V, fp64.
+
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d]; do: dL/dO, [B, Hq, Nq, d].
+    Returns (dQ [B, Hq, Nq, d], dK [B, Hkv, Nk, d], dV [B, Hkv, Nk, d]).
+
+    Per (b, h), with P the row softmax of the (masked) scaled scores, taken
+    from the same three-pass softmax as ``attention``:
+      dV  = P^T dO                              (O is linear in V)
+      dP  = dO V^T
+      dS  = P * (dP - rowsum(P * dP))           (the softmax Jacobian:
+                                                 dP_ij -> P_ij (dP_ij - sum_k P_ik dP_ik))
+      dQ  = scale * dS K,    dK = scale * dS^T Q
+    Masked scores have P = 0 and so no gradient; a row that sees no key has
+    zero gradients. A KV head shared by a group of query heads collects the
+    sum of their dK and dV (the chain rule through the shared tensor).
+    The forward statistics the GPU path saves (LSE) and its row sums
+    rowsum(dO * O) are the same quantities up to rounding; the oracle does
+    not use them.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if do.shape != q.shape or v.shape != k.shape or Hq % Hkv != 0:
+        raise ValueError("shape mismatch")
+    group = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if Nq == 0 or Nk == 0:
+        return dq, dk, dv
+    vis = _visible(np.arange(Nq), Nq, Nk) if causal else None
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // group
+            S = scale * (q[b, h] @ k[b, hk].T)                  # [Nq, Nk]
+            if vis is not None:
+                S = np.where(vis, S, -np.inf)
+            m = np.max(S, axis=1)
+            live = m > -np.inf
+            E = np.zeros_like(S)
+            E[live] = np.exp(S[live] - m[live, None])
+            l = np.sum(E, axis=1)
+            P = np.zeros_like(S)
+            P[live] = E[live] / l[live, None]
+            dv[b, hk] += P.T @ do[b, h]
+            dP = do[b, h] @ v[b, hk].T
+            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            dq[b, h] = scale * (dS @ k[b, hk])
+            dk[b, hk] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv

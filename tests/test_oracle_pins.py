@@ -453,3 +453,132 @@ def test_fp8_dequantisation_and_scales():
     assert np.max(np.abs(l3 - lse)) < 1e-13
     o4, l4 = oracle.attention_fp8(qc, kc, vc, 1.0, sq * sk, sv, 0.5)
     assert np.max(np.abs(o4 - o)) < 1e-13
+
+
+# ---------------------------------------------------------------- backward
+# The gradient of the definition is pinned by numerical differentiation of
+# the forward oracle (central differences in fp64 on tiny inputs, an
+# independent route to the same derivative) and by invariants of the
+# softmax that a dropped term, a wrong sign or a transposed operand breaks.
+def _loss_grad_fd(q, k, v, g, scale, causal, eps=1e-6):
+    """Central-difference gradients of L = sum(O * g) w.r.t. q, k, v."""
+    def loss(q_, k_, v_):
+        o, _ = oracle.attention(q_, k_, v_, scale, causal=causal)
+        return float(np.sum(o * g))
+    out = []
+    for x in (q, k, v):
+        gx = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[i] += eps
+            xm[i] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            idx = [q is x, k is x, v is x].index(True)
+            args_p[idx], args_m[idx] = xp, xm
+            gx[i] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        out.append(gx)
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal", [
+    (1, 1, 1, 4, 5, 3, False),
+    (1, 2, 1, 5, 5, 3, True),      # GQA, causal square
+    (2, 2, 2, 3, 6, 2, True),      # causal, Nk > Nq (bottom-right)
+    (1, 1, 1, 6, 3, 2, True),      # causal, Nq > Nk: rows 0..2 see no key
+])
+def test_backward_matches_finite_differences(B, Hq, Hkv, Nq, Nk, d, causal):
+    rng = np.random.default_rng(7 + Nq * Nk)
+    q = rng.standard_normal((B, Hq, Nq, d))
+    k = rng.standard_normal((B, Hkv, Nk, d))
+    v = rng.standard_normal((B, Hkv, Nk, d))
+    g = rng.standard_normal((B, Hq, Nq, d))
+    scale = 0.7
+    dq, dk, dv = oracle.attention_backward(q, k, v, g, scale, causal=causal)
+    fq, fk, fv = _loss_grad_fd(q, k, v, g, scale, causal)
+    for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+        assert np.max(np.abs(a - b)) < 1e-7
+
+
+def test_backward_key_shift_gives_zero_key_gradient_sum():
+    # adding u to every key adds scale*q_i.u to every visible score of row i:
+    # the softmax is unchanged, so sum_j dK_j = 0 (for every KV head)
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((2, 4, 33, 8))
+    k = rng.standard_normal((2, 2, 40, 8))
+    v = rng.standard_normal((2, 2, 40, 8))
+    g = rng.standard_normal((2, 4, 33, 8))
+    for causal in (False, True):
+        _, dk, _ = oracle.attention_backward(q, k, v, g, 0.3, causal=causal)
+        assert np.max(np.abs(dk.sum(axis=2))) < 1e-12
+
+
+def test_backward_equal_keys_give_zero_dq():
+    # all keys equal: every score of a row is the same, P is uniform
+    # whatever Q is, so dQ = 0 (and dV_j = mean over rows of dO)
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 1, 7, 5))
+    k = np.repeat(rng.standard_normal((1, 1, 1, 5)), 9, axis=2)
+    v = rng.standard_normal((1, 1, 9, 5))
+    g = rng.standard_normal((1, 1, 7, 5))
+    dq, _, dv = oracle.attention_backward(q, k, v, g, 0.5)
+    assert np.max(np.abs(dq)) < 1e-12
+    want = np.repeat(g.sum(axis=2, keepdims=True) / 9, 9, axis=2)
+    assert np.max(np.abs(dv - want)) < 1e-12
+
+
+def test_backward_scale_placement():
+    # f(Q; s) = f(s Q; 1): dQ at scale s is s times dQ at scale 1 taken at
+    # s Q, and dK at scale s equals dK at scale 1 taken at s Q
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 2, 6, 4))
+    k = rng.standard_normal((1, 2, 8, 4))
+    v = rng.standard_normal((1, 2, 8, 4))
+    g = rng.standard_normal((1, 2, 6, 4))
+    s = 0.37
+    dq_s, dk_s, dv_s = oracle.attention_backward(q, k, v, g, s, causal=True)
+    dq_1, dk_1, dv_1 = oracle.attention_backward(s * q, k, v, g, 1.0,
+                                                 causal=True)
+    assert np.max(np.abs(dq_s - s * dq_1)) < 1e-12
+    assert np.max(np.abs(dk_s - dk_1)) < 1e-12
+    assert np.max(np.abs(dv_s - dv_1)) < 1e-12
+
+
+def test_backward_gqa_is_sum_over_repeated_heads():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 6, 5, 3))
+    k = rng.standard_normal((1, 2, 7, 3))
+    v = rng.standard_normal((1, 2, 7, 3))
+    g = rng.standard_normal((1, 6, 5, 3))
+    dq, dk, dv = oracle.attention_backward(q, k, v, g, 0.9, causal=True)
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+    dq2, dk2, dv2 = oracle.attention_backward(q, kr, vr, g, 0.9, causal=True)
+    assert np.max(np.abs(dq - dq2)) < 1e-12
+    assert np.max(np.abs(dk - dk2.reshape(1, 2, 3, 7, 3).sum(axis=2))) < 1e-12
+    assert np.max(np.abs(dv - dv2.reshape(1, 2, 3, 7, 3).sum(axis=2))) < 1e-12
+
+
+def test_backward_linear_in_upstream_gradient():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 1, 6, 4))
+    k = rng.standard_normal((1, 1, 6, 4))
+    v = rng.standard_normal((1, 1, 6, 4))
+    g1 = rng.standard_normal((1, 1, 6, 4))
+    g2 = rng.standard_normal((1, 1, 6, 4))
+    a = oracle.attention_backward(q, k, v, g1, 0.5)
+    b = oracle.attention_backward(q, k, v, g2, 0.5)
+    c = oracle.attention_backward(q, k, v, 2.0 * g1 - 3.0 * g2, 0.5)
+    for x, y, z in zip(a, b, c):
+        assert np.max(np.abs(z - (2.0 * x - 3.0 * y))) < 1e-12
+
+
+def test_backward_rows_without_keys_have_zero_gradient():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 1, 6, 3))
+    k = rng.standard_normal((1, 1, 3, 3))
+    v = rng.standard_normal((1, 1, 3, 3))
+    g = rng.standard_normal((1, 1, 6, 3))
+    dq, _, _ = oracle.attention_backward(q, k, v, g, 1.0, causal=True)
+    assert np.all(dq[0, 0, :3] == 0) and np.any(dq[0, 0, 3:] != 0)
