@@ -1,4 +1,4 @@
-"""MI355X (gfx950) exact attention: fused prefill forward and paged decode.
+"""MI355X (gfx950) exact attention: fused forward, backward and paged decode.
 
 The computation lives in ``libfa.so`` (hand-written HIP kernels behind the
 C ABI of ``include/fa.h``); this package only binds it. Build it in-tree
@@ -11,10 +11,12 @@ from ._lib import (  # noqa: F401
     FA_DTYPE_FP8_E4M3,
     FaError,
     LIB_PATH,
+    fa_bwd,
+    fa_bwd_workspace_size,
     fa_fwd,
     fa_paged_decode,
     fa_paged_decode_workspace_size,
     fa_strerror,
     load_library,
 )
-from .api import attention, paged_decode  # noqa: F401
+from .api import attention, attention_backward, paged_decode  # noqa: F401

@@ -31,8 +31,8 @@ FA_ESPLITS = -10
 FA_EALIGN = -11
 
 # every function include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_paged_decode", "fa_paged_decode_workspace_size",
-           "fa_strerror")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
+           "fa_paged_decode_workspace_size", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -57,6 +57,10 @@ def load_library(path: str = LIB_PATH):
     lib.fa_fwd.restype = i
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
                            vp, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, i, vp, sz, vp]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_paged_decode.restype = i
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                     f, vp, vp, vp, sz, i, vp]
@@ -111,6 +115,26 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype,
                       float(scale), int(bool(causal)), int(dtype),
                       ctypes.cast(desc, ctypes.c_void_p) if desc else None,
                       _stream(stream, q, o))
+    if check:
+        _check(code)
+    return code
+
+
+def fa_bwd_workspace_size(B, Hq, Nq) -> int:
+    return int(load_library().fa_bwd_workspace_size(int(B), int(Hq), int(Nq)))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+           causal, dtype, workspace, workspace_bytes, stream=None,
+           check=True) -> int:
+    """Exact attention backward (see include/fa.h)."""
+    lib = load_library()
+    code = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), int(B),
+                      int(Hq), int(Hkv), int(Nq), int(Nk), int(d),
+                      float(scale), int(bool(causal)), int(dtype),
+                      _ptr(workspace), int(workspace_bytes),
+                      _stream(stream, q, dq))
     if check:
         _check(code)
     return code

@@ -63,3 +63,26 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, scale=None,
                          workspace.numel() * workspace.element_size(),
                          num_splits, stream)
     return out, lse
+
+
+def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None,
+                       dq=None, dk=None, dv=None, workspace=None,
+                       stream=None):
+    """dQ, dK, dV (bf16) of exact attention, from the forward's o and lse
+    and the upstream gradient dout; P is re-computed in the kernels."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = _lib.fa_bwd_workspace_size(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8,
+                                device=q.device)
+    _lib.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d,
+                scale, causal, _dtype_code(q), workspace,
+                workspace.numel() * workspace.element_size(), stream)
+    return dq, dk, dv

@@ -115,6 +115,64 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return (int)e;
 }
 
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0) return 0;
+  if (numel4(B, Hq, Nq, 1) < 0 || (long)B * Hq * Nq > kMaxIndex * 64L) return 0;
+  return fa::bwd_workspace_bytes(B, Hq, Nq);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+           int causal, int dtype, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return FA_EINVAL_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_EINVAL_DIM;
+  if (d != 64 && d != 128) return FA_EUNSUPPORTED_D;
+  if (Hq % Hkv != 0) return FA_EGQA;
+  if (dtype != FA_DTYPE_BF16) return FA_EDTYPE;
+  if (!(isfinite(scale) && scale > 0.f)) return FA_ESCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      ((uintptr_t)lse & 3u) != 0)
+    return FA_EALIGN;
+  if ((long)Nq * d > kMaxIndex || (long)Nk * d > kMaxIndex) return FA_EINVAL_DIM;
+  if (numel4(B, Hq, Nq, d) < 0 || numel4(B, Hkv, Nk, d) < 0) return FA_EINVAL_DIM;
+  long blocks;
+  if (!mul_ok((Nq + 127) / 128, (long)Hq * B, &blocks) || blocks > kMaxIndex)
+    return FA_EINVAL_DIM;
+  if (!mul_ok((Nk + 127) / 128, (long)Hkv * B, &blocks) || blocks > kMaxIndex)
+    return FA_EINVAL_DIM;
+  if ((long)B * Hq * Nq * (d / 8) / 256 > kMaxIndex) return FA_EINVAL_DIM;
+  const size_t need = fa_bwd_workspace_size(B, Hq, Nq);
+  if (need == 0) return FA_EINVAL_DIM;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return FA_EWORKSPACE;
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.ws = workspace;
+  a.stream = static_cast<hipStream_t>(stream);
+  return (int)fa::launch_bwd_bf16(a);
+}
+
 static int decode_check(int B, int Hq, int Hkv, int d, int max_pages,
                         int page_size, int num_splits) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_pages <= 0) return FA_EINVAL_DIM;

@@ -21,6 +21,25 @@ struct FwdArgs {
   hipStream_t stream;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  bool causal;
+  void* ws;  // row sums D and log2-scaled LSE
+  hipStream_t stream;
+};
+size_t bwd_workspace_bytes(int B, int Hq, int Nq);
+hipError_t launch_bwd_bf16(const BwdArgs& a);
+
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_fp8(const FwdArgs& a);

@@ -6,6 +6,8 @@
  * the probability matrix P never reach device memory:
  *
  *   fa_fwd           prefill / training forward over contiguous Q, K, V.
+ *   fa_bwd           training backward: dQ, dK, dV from the forward's O and
+ *                    LSE, with P re-computed on chip (never stored).
  *   fa_paged_decode  one query token per request against a paged KV cache,
  *                    split over workgroups and merged by log-sum-exp.
  *
@@ -108,6 +110,44 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
            int causal, int dtype, const float* qkv_descale, void* stream);
+
+/*
+ * fa_bwd_workspace_size - bytes of device workspace fa_bwd needs for
+ * B * Hq * Nq query rows (two fp32 values per row plus padding); 0 when a
+ * size is not positive. Contents on entry do not matter.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq);
+
+/*
+ * fa_bwd - exact attention backward ([Capstone §6.1], the row about writing
+ * P to HBM, and §7.3 question 1: the forward keeps no P, so the backward
+ * re-computes it on chip from Q, K and the saved row statistics).
+ *
+ * With S, P the scaled scores and probabilities of fa_fwd (same mask) and
+ * dO = dL/dO, computes the gradient of the definition:
+ *   dV[b,g] = sum over the query heads h of group g of P^T dO
+ *   dQ[b,h] = scale * dS K,   dK[b,g] = scale * sum_h dS^T Q,
+ *   dS = P * (dP - D),  dP = dO V^T,  D_i = sum_d dO[i,d] * O[i,d]
+ * where P_ij = exp(S_ij - LSE_i) is re-computed from Q, K and the LSE that
+ * fa_fwd returned. Deterministic (no atomics).
+ *
+ * q, o, dout  [B, Hq,  Nq, d] bf16 (o: the forward's output)
+ * k, v        [B, Hkv, Nk, d] bf16
+ * lse         [B, Hq,  Nq] fp32, the forward's LSE (-inf rows get zero
+ *             gradients)
+ * dq          [B, Hq,  Nq, d] bf16, written (fp32 accumulation, rounded once)
+ * dk, dv      [B, Hkv, Nk, d] bf16, written
+ * Hq % Hkv == 0; scale finite and > 0; causal as in fa_fwd.
+ * dtype       FA_DTYPE_BF16 (the only one supported; others -> FA_EDTYPE)
+ * workspace   device memory of at least fa_bwd_workspace_size(B, Hq, Nq)
+ *             bytes, 256-byte aligned; workspace_bytes its true size.
+ * stream      hipStream_t or NULL.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+           int causal, int dtype, void* workspace, size_t workspace_bytes,
+           void* stream);
 
 /*
  * fa_paged_decode_workspace_size - bytes of device workspace that

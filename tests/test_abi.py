@@ -106,6 +106,50 @@ def test_fwd_raises_with_message(lib):
     assert "64 or 128" in str(e.value)
 
 
+def bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4,
+             Hkv=2, Nq=8, Nk=8, d=128, scale=0.1, causal=0,
+             dtype=L.FA_DTYPE_BF16, workspace=P, workspace_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return fa.fa_bwd(**a, check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), L.FA_EINVAL_NULL),
+    (dict(dout=None), L.FA_EINVAL_NULL),
+    (dict(lse=None), L.FA_EINVAL_NULL),
+    (dict(dq=None), L.FA_EINVAL_NULL),
+    (dict(dv=None), L.FA_EINVAL_NULL),
+    (dict(B=0), L.FA_EINVAL_DIM),
+    (dict(Nk=0), L.FA_EINVAL_DIM),
+    (dict(d=32), L.FA_EUNSUPPORTED_D),
+    (dict(Hq=6, Hkv=4), L.FA_EGQA),
+    (dict(dtype=L.FA_DTYPE_F32), L.FA_EDTYPE),
+    (dict(dtype=L.FA_DTYPE_FP8_E4M3), L.FA_EDTYPE),
+    (dict(scale=float("nan")), L.FA_ESCALE),
+    (dict(dk=P + 8), L.FA_EALIGN),
+    (dict(lse=P + 1), L.FA_EALIGN),
+    (dict(workspace=None), L.FA_EWORKSPACE),
+    (dict(workspace_bytes=64), L.FA_EWORKSPACE),
+    (dict(workspace=P + 64), L.FA_EWORKSPACE),
+    (dict(Nq=1 << 25), L.FA_EINVAL_DIM),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_workspace_size(lib):
+    # two fp32 arrays of B*Hq*Nq rows, each with at least 32 rows of padding,
+    # rounded up to 64 rows (the documented layout)
+    up = lambda x: -(-(x + 32) // 64) * 64
+    assert fa.fa_bwd_workspace_size(1, 1, 1) == 8 * up(1)
+    assert fa.fa_bwd_workspace_size(2, 16, 2048) == 8 * up(2 * 16 * 2048)
+    assert fa.fa_bwd_workspace_size(1, 32, 16384) == 8 * up(32 * 16384)
+    assert fa.fa_bwd_workspace_size(0, 1, 1) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, -5) == 0
+
+
 def dec(**kw):
     a = dict(q=P, k_pool=P, v_pool=P, block_table=P, seq_lens=P, page_size=16,
              num_pages=100, B=4, Hq=32, Hkv=8, d=128, max_pages_per_seq=512,

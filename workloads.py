@@ -172,3 +172,11 @@ def decode_config(name, seed=42) -> DecodeInputs:
 def as_f64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a storage tensor to fp64 numpy (values unchanged)."""
     return t.to(torch.float64).numpy()
+
+
+def upstream_grad(shape, seed=4242, dtype="bf16") -> torch.Tensor:
+    """dL/dO for the backward tests: i.i.d. N(0, 1) in fp32, cast."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal(tuple(shape), dtype=np.float32)
+    t, _ = _to_storage(g, dtype)
+    return t
