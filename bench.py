@@ -6,15 +6,19 @@ One step = one pass of the whole path over its synthetic workloads:
   2. paged-KV decode, 64 requests, lengths U{512..8192}, page 16,
      Hq=32, Hkv=8, d=128 (fa_paged_decode: split kernel + merge kernel)
   3. fp8 e4m3 prefill, B=2, H=16, N=8192, d=128, non-causal (fa_fwd)
+  4. the backward of workload 1 (fa_bwd: dQ, dK, dV from O, LSE and a
+     seeded dO)
 Inputs are seeded N(0,1) draws (seed 42) already resident in HBM when the
 timed region starts. Each launch is bracketed by HIP events on the stream
-it runs on; the step time is the wall time of K steps between two device
-synchronisations.
+it runs on; the step time is the wall time of K steps of legs 1-3 between
+two device synchronisations. Leg 4 is timed afterwards, K launches of its
+own.
 
 Prints ONE JSON line. `value` is the bf16 causal prefill throughput in
 TFLOPS (algorithmic FLOPs: 4*d per visible (query, key) pair per query
-head; causal counts N(N+1)/2 pairs). The decode and fp8 legs are reported
-in their own objects (GB/s of algorithmic KV bytes, TFLOPS).
+head; causal counts N(N+1)/2 pairs). The decode, fp8 and backward legs are
+reported in their own objects (GB/s of algorithmic KV bytes, TFLOPS; the
+backward counts 10*d FLOPs per visible pair: five products).
 """
 from __future__ import annotations
 
@@ -141,7 +145,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,fp8",
+    ap.add_argument("--legs", default="prefill,decode,fp8,bwd",
                     help="comma list of legs to run (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -202,33 +206,70 @@ def main():
         q8, k8, v8 = (t.to(dev) for t in (inp.q, inp.k, inp.v))
         o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
         l8 = torch.empty(q8.shape[:3], dtype=torch.float32, device=dev)
-        calls["fp8"] = lambda: fa.fa_fwd(
+        calls["fp8"] = lambda c=c, inp=inp: fa.fa_fwd(
             q8, k8, v8, o8, l8, c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"],
             c["d"], inp.scale, False, fa.FA_DTYPE_FP8_E4M3, inp.descale,
             stream)
         info["fp8"] = dict(flops=prefill_flops(c), cfg=c)
+    if "bwd" in legs:
+        # backward of the causal GQA prefill: O and LSE from one forward
+        # call outside the timed region, dO seeded
+        cb = W.PREFILL_CONFIGS[PREFILL]
+        ib = W.prefill_config(PREFILL)
+        qb, kb, vb = (t.to(dev) for t in (ib.q, ib.k, ib.v))
+        gb = W.upstream_grad(tuple(ib.q.shape), seed=43).to(dev)
+        ob = torch.empty(qb.shape, dtype=torch.bfloat16, device=dev)
+        lb = torch.empty(qb.shape[:3], dtype=torch.float32, device=dev)
+        fa.fa_fwd(qb, kb, vb, ob, lb, cb["B"], cb["Hq"], cb["Hkv"], cb["Nq"],
+                  cb["Nk"], cb["d"], ib.scale, True, fa.FA_DTYPE_BF16, None,
+                  stream)
+        dqb, dkb, dvb = (torch.empty_like(t) for t in (qb, kb, vb))
+        wsb = torch.empty(fa.fa_bwd_workspace_size(cb["B"], cb["Hq"], cb["Nq"]),
+                          dtype=torch.uint8, device=dev)
+        calls["bwd"] = lambda cb=cb, ib=ib: fa.fa_bwd(
+            qb, kb, vb, ob, gb, lb, dqb, dkb, dvb, cb["B"], cb["Hq"],
+            cb["Hkv"], cb["Nq"], cb["Nk"], cb["d"], ib.scale, True,
+            fa.FA_DTYPE_BF16, wsb, wsb.numel(), stream)
+        # five products of 2*d FLOPs per visible pair (S re-computed, dP,
+        # dV, dQ, dK): 2.5 times the forward's work
+        info["bwd"] = dict(flops=2.5 * prefill_flops(cb), cfg=cb)
     torch.cuda.synchronize()
     print(f"bench: inputs resident, legs={legs}", file=sys.stderr, flush=True)
 
+    # the step: the forward hot path (prefill, decode, fp8); the backward
+    # leg is timed after it in a phase of its own, so its heat and power
+    # draw do not change the clocks the forward legs run at
     order = [x for x in ("prefill", "decode", "fp8", "copy") if x in calls]
+    extra = [x for x in ("bwd",) if x in calls]
+
+    def timed(names, steps):
+        ev = {n: [] for n in names}
+        for _ in range(steps):
+            for name in names:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                calls[name]()
+                e1.record(stream)
+                ev[name].append((e0, e1))
+        return ev
+
     for _ in range(args.warmup):
         for name in order:
             calls[name]()
     torch.cuda.synchronize()
-
-    ev = {n: [] for n in order}
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        for name in order:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            calls[name]()
-            e1.record(stream)
-            ev[name].append((e0, e1))
+    ev = timed(order, args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if extra:
+        for _ in range(args.warmup):
+            for name in extra:
+                calls[name]()
+        torch.cuda.synchronize()
+        ev.update(timed(extra, args.steps))
+        torch.cuda.synchronize()
+        order = order + extra
     ms = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in order}
     print("bench: timed region done " + ", ".join(
         f"{n}={statistics.mean(ms[n]):.3f}ms" for n in order),
@@ -287,6 +328,19 @@ def main():
             "launch_ms_mean": t * 1e3}
         workload.append(f"fp8 e4m3 prefill B={c['B']} H={c['Hq']} N={c['Nq']} "
                         f"d={c['d']}")
+        if "value" not in out:
+            out["value"], out["unit"] = tf, "TFLOPS"
+    if "bwd" in order:
+        c = info["bwd"]["cfg"]
+        t = statistics.mean(ms["bwd"]) / 1e3
+        tf = info["bwd"]["flops"] / t / 1e12
+        out["backward"] = {
+            "value": tf, "unit": "TFLOPS", "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+            "algorithmic_gflop_per_launch": info["bwd"]["flops"] / 1e9,
+            "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel",
+            "launch_ms_mean": t * 1e3, "launch_ms_min": min(ms["bwd"])}
+        workload.append(f"bf16 causal GQA backward B={c['B']} Hq={c['Hq']} "
+                        f"Hkv={c['Hkv']} N={c['Nq']} d={c['d']}")
         if "value" not in out:
             out["value"], out["unit"] = tf, "TFLOPS"
     if "copy" in order:

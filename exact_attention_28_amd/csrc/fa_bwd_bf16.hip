@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 
 // -------------------------------------------------------------- dK, dV
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
     const float* __restrict__ Dv, const float* __restrict__ L2,
@@ -133,6 +133,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     int Nq, int Nk, float c, float scale) {
   constexpr int BR = 32;  // query rows per tile
   using T = RowTile<D, BR>;
+  using TV = RowTile<D, 128>;
+  // the workgroup's 128 V rows, read as B operands every tile (holding
+  // them in registers as well as K would leave one wave per SIMD)
+  __shared__ __attribute__((aligned(16))) char v_lds[TV::BYTES];
   __shared__ __attribute__((aligned(16))) char q_lds0[T::BYTES];
   __shared__ __attribute__((aligned(16))) char q_lds1[T::BYTES];
   __shared__ __attribute__((aligned(16))) char o_lds0[T::BYTES];
@@ -171,14 +175,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int keyc = min(key, Nk - 1);
   const int off = Nk - Nq;
 
-  // this wave's 32 keys as B operands (lane: key r32, d = 16s + 8h + t)
+  // this wave's 32 keys of K as B operands (lane: key r32, d = 16s + 8h +
+  // t); the workgroup's 128 V rows go to LDS
   const long kvbase = (long)(ti.b * Hkv + hk) * Nk * D;
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
+  for (int s = 0; s < D / 16; ++s)
     kf[s] = *reinterpret_cast<const bf16x8*>(K + kvbase + (long)keyc * D + 16 * s + 8 * h);
-    vf[s] = *reinterpret_cast<const bf16x8*>(V + kvbase + (long)keyc * D + 16 * s + 8 * h);
-  }
+  load_tile<D, 128>(V + kvbase, k0, Nk, (lds_char*)v_lds, w, lane);
+  const lds_char* vrow = (const lds_char*)v_lds + TV::row_off(32 * w + r32) + 16 * h;
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
@@ -210,14 +215,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // per-lane fragment offsets in a tile: row r32 (+16 bytes for h); the
   // transposed operand's rows 16j + 8e + 4h + i16/4 at column bytes
   // 2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3))
+  // (row_off(r0 + x) = row_off(r0) + row_off(x) for the r0 used with x < 8,
+  // so each is one base register plus compile-time offsets)
   const int rfrag = T::row_off(r32) + 16 * h;
-  int tfrag[2][2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      tfrag[j][e] = T::row_off(16 * j + 8 * e + 4 * h + (i16 >> 2)) +
+  const int tbase = T::row_off(4 * h + (i16 >> 2)) +
                     2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3));
+  auto tfrag = [&](int j, int e) { return tbase + T::row_off(16 * j + 8 * e); };
 
   constexpr std::integral_constant<int, 0> B0{};
   constexpr std::integral_constant<int, 1> B1{};
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int sd = 0; sd < D / 16; ++sd) {
       s = mfma_32x32x16_bf16(lds_row16(qp + rfrag + 32 * sd), kf[sd], s);
-      p = mfma_32x32x16_bf16(lds_row16(op + rfrag + 32 * sd), vf[sd], p);
+      p = mfma_32x32x16_bf16(lds_row16(op + rfrag + 32 * sd), lds_row16(vrow + 32 * sd), p);
     }
     // P and dS per element; rows past Nq and causally hidden pairs get 0
     const lds_char* sp = sbuf(cur);
@@ -263,8 +266,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         float sv = s[v];
         if (need_mask) {
           const int i = i0 + 8 * gq + 4 * h + e;
-          const bool vis = i < Nq && (!CAUSAL || key <= i + off);
-          if (!vis) sv = kNegInf;
+          const bool vis = (i < Nq) & (!CAUSAL | (key <= i + off));
+          sv = vis ? sv : kNegInf;
         }
         pv[e] = fast_exp2(__builtin_fmaf(sv, c, -l2[e]));
         dv4[e] = pv[e] * (p[v] - dr[e]);
@@ -284,9 +287,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
         dv[mb] = mfma_32x32x16_bf16(
-            lds_tr16(op + tfrag[j][0] + 64 * mb, op + tfrag[j][1] + 64 * mb), pb, dv[mb]);
+            lds_tr16(op + tfrag(j, 0) + 64 * mb, op + tfrag(j, 1) + 64 * mb), pb, dv[mb]);
         dk[mb] = mfma_32x32x16_bf16(
-            lds_tr16(qp + tfrag[j][0] + 64 * mb, qp + tfrag[j][1] + 64 * mb), db, dk[mb]);
+            lds_tr16(qp + tfrag(j, 0) + 64 * mb, qp + tfrag(j, 1) + 64 * mb), db, dk[mb]);
       }
     }
   };
@@ -376,17 +379,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   // fragment offsets: K/V rows 32kb + r32 (+16 bytes for h); K^T rows
   // 32kb + 16j + 8e + 4h + i16/4 at column bytes 2*(16*((lane>>4)&1) + 4*(i16&3))
-  int rfrag[2], tfrag[2][2][2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    rfrag[kb] = T::row_off(32 * kb + r32) + 16 * h;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        tfrag[kb][j][e] = T::row_off(32 * kb + 16 * j + 8 * e + 4 * h + (i16 >> 2)) +
-                          2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3));
-  }
+  // (row_off(r0 + x) = row_off(r0) + row_off(x) for the r0 used here, so
+  // each offset is one base register plus a compile-time constant)
+  const int rbase = T::row_off(r32) + 16 * h;
+  const int tbase = T::row_off(4 * h + (i16 >> 2)) +
+                    2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3));
+  auto rfrag = [&](int kb) { return rbase + T::row_off(32 * kb); };
+  auto tfrag = [&](int kb, int j, int e) {
+    return tbase + T::row_off(32 * kb + 16 * j + 8 * e);
+  };
 
   auto issue = [&](int tile, auto buf) {
     load_tile<D, BN>(Kh, BN * tile, Nk, kbuf(buf), w, lane);
@@ -421,8 +422,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     for (int sd = 0; sd < D / 16; ++sd)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma_32x32x16_bf16(lds_row16(kp + rfrag[kb] + 32 * sd), qf[sd], s[kb]);
-        p[kb] = mfma_32x32x16_bf16(lds_row16(vp + rfrag[kb] + 32 * sd), of[sd], p[kb]);
+        s[kb] = mfma_32x32x16_bf16(lds_row16(kp + rfrag(kb) + 32 * sd), qf[sd], s[kb]);
+        p[kb] = mfma_32x32x16_bf16(lds_row16(vp + rfrag(kb) + 32 * sd), of[sd], p[kb]);
       }
     const bool need_mask = (n0 + BN > Nk) || (CAUSAL && n0 + BN - 1 > wrow0 + off);
     const int lim = CAUSAL ? min(Nk - 1, row + off) : Nk - 1;
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
           acc[mb] = mfma_32x32x16_bf16(
-              lds_tr16(kp + tfrag[kb][j][0] + 64 * mb, kp + tfrag[kb][j][1] + 64 * mb),
+              lds_tr16(kp + tfrag(kb, j, 0) + 64 * mb, kp + tfrag(kb, j, 1) + 64 * mb),
               db, acc[mb]);
       }
   };
