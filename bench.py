@@ -8,11 +8,12 @@ One step = one pass of the whole path over its synthetic workloads:
   3. fp8 e4m3 prefill, B=2, H=16, N=8192, d=128, non-causal (fa_fwd)
   4. the backward of workload 1 (fa_bwd: dQ, dK, dV from O, LSE and a
      seeded dO)
+  5. workload 2 over a cache stored as e4m3 codes (fa_paged_decode_fp8kv)
 Inputs are seeded N(0,1) draws (seed 42) already resident in HBM when the
 timed region starts. Each launch is bracketed by HIP events on the stream
 it runs on; the step time is the wall time of K steps of legs 1-3 between
-two device synchronisations. Leg 4 is timed afterwards, K launches of its
-own.
+two device synchronisations. Legs 4 and 5 are timed afterwards, K
+launches each.
 
 Prints ONE JSON line. `value` is the bf16 causal prefill throughput in
 TFLOPS (algorithmic FLOPs: 4*d per visible (query, key) pair per query
@@ -56,12 +57,12 @@ def prefill_flops(c):
     return 4.0 * c["d"] * pairs * c["Hq"] * c["B"]
 
 
-def decode_bytes(di, Hkv, d):
+def decode_bytes(di, Hkv, d, kv_elem_bytes=2):
     """K and V of every cached token read once per KV head (the query heads
     of a group share them), plus q, o, LSE and the block-table entries."""
     import torch
     L = di.seq_lens.to(torch.int64)
-    kv = int(L.sum()) * Hkv * d * 2 * 2
+    kv = int(L.sum()) * Hkv * d * 2 * kv_elem_bytes
     B, Hq, _ = di.q.shape
     pages = int(((L + di.page_size - 1) // di.page_size).sum())
     return kv + B * Hq * d * 2 * 2 + B * Hq * 4 + pages * 4
@@ -145,7 +146,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,fp8,bwd",
+    ap.add_argument("--legs", default="prefill,decode,fp8,bwd,decode8",
                     help="comma list of legs to run (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -233,6 +234,24 @@ def main():
         # five products of 2*d FLOPs per visible pair (S re-computed, dP,
         # dV, dQ, dK): 2.5 times the forward's work
         info["bwd"] = dict(flops=2.5 * prefill_flops(cb), cfg=cb)
+    if "decode8" in legs:
+        # the same decode over the cache stored as e4m3 codes + two scales
+        d8 = W.decode_config(DECODE, kv_dtype="fp8")
+        q8d = d8.q.to(dev)
+        kp8, vp8 = d8.k_pool.to(dev), d8.v_pool.to(dev)
+        bt8, sl8 = d8.block_table.to(dev), d8.seq_lens.to(dev)
+        B8, Hq8, dd8 = q8d.shape
+        np8, pg8, Hkv8, _ = kp8.shape
+        mp8 = bt8.shape[1]
+        ws8 = torch.empty(fa.fa_paged_decode_workspace_size(
+            B8, Hq8, Hkv8, dd8, mp8, pg8, 0), dtype=torch.uint8, device=dev)
+        od8 = torch.empty((B8, Hq8, dd8), dtype=torch.bfloat16, device=dev)
+        ld8 = torch.empty((B8, Hq8), dtype=torch.float32, device=dev)
+        calls["decode8"] = lambda: fa.fa_paged_decode_fp8kv(
+            q8d, kp8, vp8, bt8, sl8, pg8, np8, B8, Hq8, Hkv8, dd8, mp8,
+            d8.scale, d8.kv_descale, od8, ld8, ws8, ws8.numel(), 0, stream)
+        info["decode8"] = dict(bytes=decode_bytes(d8, Hkv8, dd8, 1),
+                               kv_tokens=int(d8.seq_lens.sum()))
     torch.cuda.synchronize()
     print(f"bench: inputs resident, legs={legs}", file=sys.stderr, flush=True)
 
@@ -240,7 +259,7 @@ def main():
     # leg is timed after it in a phase of its own, so its heat and power
     # draw do not change the clocks the forward legs run at
     order = [x for x in ("prefill", "decode", "fp8", "copy") if x in calls]
-    extra = [x for x in ("bwd",) if x in calls]
+    extra = [x for x in ("bwd", "decode8") if x in calls]
 
     def timed(names, steps):
         ev = {n: [] for n in names}
@@ -343,6 +362,18 @@ def main():
                         f"Hkv={c['Hkv']} N={c['Nq']} d={c['d']}")
         if "value" not in out:
             out["value"], out["unit"] = tf, "TFLOPS"
+    if "decode8" in order:
+        t = statistics.mean(ms["decode8"]) / 1e3
+        gbs = info["decode8"]["bytes"] / t / 1e9
+        out["decode_fp8_cache"] = {
+            "value": gbs, "unit": "GB/s", "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+            "kernel": "decode_kernel<e4m3 cache> + decode_merge_kernel",
+            "algorithmic_bytes": info["decode8"]["bytes"],
+            "tokens_per_s": info["decode8"]["kv_tokens"] / t,
+            "launch_ms_mean": t * 1e3, "launch_ms_min": min(ms["decode8"])}
+        workload.append("paged decode over an e4m3 cache (same requests)")
+        if "value" not in out:
+            out["value"], out["unit"] = gbs, "GB/s"
     if "copy" in order:
         t = statistics.mean(ms["copy"]) / 1e3
         out["copy_calibration"] = {"bytes_per_launch": info["copy"]["bytes"],

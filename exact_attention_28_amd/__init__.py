@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     fa_bwd_workspace_size,
     fa_fwd,
     fa_paged_decode,
+    fa_paged_decode_fp8kv,
     fa_paged_decode_workspace_size,
     fa_strerror,
     load_library,

@@ -32,7 +32,8 @@ FA_EALIGN = -11
 
 # every function include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
-           "fa_paged_decode_workspace_size", "fa_strerror")
+           "fa_paged_decode_fp8kv", "fa_paged_decode_workspace_size",
+           "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -64,6 +65,9 @@ def load_library(path: str = LIB_PATH):
     lib.fa_paged_decode.restype = i
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                     f, vp, vp, vp, sz, i, vp]
+    lib.fa_paged_decode_fp8kv.restype = i
+    lib.fa_paged_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i,
+                                          i, i, f, vp, vp, vp, vp, sz, i, vp]
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_strerror.restype = ctypes.c_char_p
@@ -157,6 +161,29 @@ def fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, page_size,
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
         _ptr(seq_lens), int(page_size), int(num_pages), int(B), int(Hq),
         int(Hkv), int(d), int(max_pages_per_seq), float(scale), _ptr(o),
+        _ptr(lse), _ptr(workspace), int(workspace_bytes), int(num_splits),
+        _stream(stream, q, o))
+    if check:
+        _check(code)
+    return code
+
+
+def fa_paged_decode_fp8kv(q, k_pool, v_pool, block_table, seq_lens,
+                          page_size, num_pages, B, Hq, Hkv, d,
+                          max_pages_per_seq, scale, kv_descale, o, lse,
+                          workspace, workspace_bytes, num_splits=0,
+                          stream=None, check=True) -> int:
+    """Paged decode over an e4m3 cache (see include/fa.h). kv_descale: two
+    floats (s_k, s_v) on the host, or None."""
+    lib = load_library()
+    desc = None
+    if kv_descale is not None:
+        desc = (ctypes.c_float * 2)(*[float(x) for x in kv_descale])
+    code = lib.fa_paged_decode_fp8kv(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        _ptr(seq_lens), int(page_size), int(num_pages), int(B), int(Hq),
+        int(Hkv), int(d), int(max_pages_per_seq), float(scale),
+        ctypes.cast(desc, ctypes.c_void_p) if desc else None, _ptr(o),
         _ptr(lse), _ptr(workspace), int(workspace_bytes), int(num_splits),
         _stream(stream, q, o))
     if check:

@@ -198,12 +198,15 @@ size_t fa_paged_decode_workspace_size(int B, int Hq, int Hkv, int d,
   return plan.workspace_bytes;
 }
 
-int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
-                    const int32_t* block_table, const int32_t* seq_lens,
-                    int page_size, int num_pages, int B, int Hq, int Hkv,
-                    int d, int max_pages_per_seq, float scale, void* o,
-                    float* lse, void* workspace, size_t workspace_bytes,
-                    int num_splits, void* stream) {
+static int paged_decode_common(const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, int page_size,
+                               int num_pages, int B, int Hq, int Hkv, int d,
+                               int max_pages_per_seq, float scale, void* o,
+                               float* lse, void* workspace,
+                               size_t workspace_bytes, int num_splits,
+                               bool kv_fp8, float s_k, float s_v,
+                               void* stream) {
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o)
     return FA_EINVAL_NULL;
   const int c = decode_check(B, Hq, Hkv, d, max_pages_per_seq, page_size,
@@ -239,8 +242,43 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
   a.o = o;
   a.lse = lse;
   a.ws = workspace;
+  a.kv_fp8 = kv_fp8;
+  a.s_k = s_k;
+  a.s_v = s_v;
   a.stream = static_cast<hipStream_t>(stream);
   return (int)fa::launch_paged_decode(a, plan);
+}
+
+int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int page_size, int num_pages, int B, int Hq, int Hkv,
+                    int d, int max_pages_per_seq, float scale, void* o,
+                    float* lse, void* workspace, size_t workspace_bytes,
+                    int num_splits, void* stream) {
+  return paged_decode_common(q, k_pool, v_pool, block_table, seq_lens,
+                             page_size, num_pages, B, Hq, Hkv, d,
+                             max_pages_per_seq, scale, o, lse, workspace,
+                             workspace_bytes, num_splits, false, 1.f, 1.f,
+                             stream);
+}
+
+int fa_paged_decode_fp8kv(const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, int page_size,
+                          int num_pages, int B, int Hq, int Hkv, int d,
+                          int max_pages_per_seq, float scale,
+                          const float* kv_descale, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          int num_splits, void* stream) {
+  if (!kv_descale) return FA_EDESCALE;
+  const float s_k = kv_descale[0], s_v = kv_descale[1];
+  if (!(isfinite(s_k) && isfinite(s_v) && s_k > 0.f && s_v > 0.f))
+    return FA_EDESCALE;
+  return paged_decode_common(q, k_pool, v_pool, block_table, seq_lens,
+                             page_size, num_pages, B, Hq, Hkv, d,
+                             max_pages_per_seq, scale, o, lse, workspace,
+                             workspace_bytes, num_splits, true, s_k, s_v,
+                             stream);
 }
 
 }  // extern "C"

@@ -21,8 +21,16 @@
 // a workgroup of Hkv waves walks the same pages in lockstep and reads each
 // page (all heads of 16 tokens, contiguous in the pool) as one block.
 //
-// Per wave and page (16 tokens of one KV head, rows of d bf16 at a stride of
-// Hkv*d):
+// The cache may also be stored as OCP e4m3 codes with per-tensor scales
+// (s_k, s_v), which halves the bytes to stream: the codes are widened
+// exactly to bf16 (K, for the MFMA) or fp32 (V, for the VALU product) in
+// registers, s_k is folded into the exp2 multiplier and s_v into the final
+// 1/l, so the arithmetic is that of the bf16 cache on the dequantised
+// values ([FA3-guide] fp8 listing for the per-tensor scales, [FA3-paged
+// §3.2] for the pages).
+//
+// Per wave and page (16 tokens of one KV head, rows of d elements at a
+// stride of Hkv*d):
 //   * S^T[token, head] = K . Q^T on v_mfma_f32_16x16x32_bf16, with K
 //     fragments loaded straight from HBM into the A operand (lane: token
 //     l%16, 16 B of d) and the group's query heads as the B operand
@@ -32,6 +40,8 @@
 //   * O[head, d] += P V on the VALU: a lane owns 4 tokens and D/16 d
 //     columns, P is broadcast inside each 16-lane row with DPP
 //     row_newbcast, V is read 16 B per lane from HBM.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -39,6 +49,7 @@ namespace fa {
 namespace {
 
 constexpr int kPage = 16;
+constexpr int kSlots8 = 2;  // pages in flight per wave, e4m3 cache
 
 // Workspace layout, in 4-byte words: T at word 0; the first and the last
 // range that touch request b at kFirstWord + b and kFirstWord + B + b; then
@@ -51,8 +62,39 @@ constexpr int kFirstWord = 64;
 // __restrict__, so the block table and lengths are read with scalar loads.
 struct KParams {
   int num_pages, B, Hq, Hkv, G, Hh, WPH, ngroups, max_pages, R;
-  float c;  // scale * log2(e)
+  float c;   // scale * log2(e) (* s_k for an e4m3 cache)
+  float sv;  // s_v for an e4m3 cache, else 1
 };
+
+// Register images of one page slot's K and V for a lane: bf16 as stored,
+// or the e4m3 codes (8 of d per K step, DL per V token row).
+template <int D, bool KV8>
+struct PageRegs;
+template <int D>
+struct PageRegs<D, false> {
+  typedef uint32_t vrow_t __attribute__((ext_vector_type(D / 32)));
+  bf16x8 k[D / 32];
+  vrow_t v[4];
+};
+template <int D>
+struct PageRegs<D, true> {
+  // K: the lane's D/4 contiguous codes, d = (D/4) * row16 + 8s + (0..7)
+  // for MFMA step s (the same permutation of d is applied to Q)
+  u32x4 k[D / 64];
+  // V: DL codes of each of the lane's 4 token rows
+  typedef uint32_t vrow_t __attribute__((ext_vector_type(D / 64)));
+  vrow_t v[4];
+};
+// e4m3 codes -> fp32 values (exact), two per conversion
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* out) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
 
 __device__ __forceinline__ int pages_of(int len, int max_len) {
   len = max(0, min(len, max_len));
@@ -106,15 +148,19 @@ struct PvAccumulate<0, GP, DL> {
                                              const float (&)[DL]) {}
 };
 
-template <int D, int GP, int NW>
+template <int D, int GP, int NW, bool KV8>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
-    KParams a, const __bf16* __restrict__ Qp, const __bf16* __restrict__ KP,
-    const __bf16* __restrict__ VP, const int32_t* __restrict__ BT,
+    KParams a, const __bf16* __restrict__ Qp, const void* __restrict__ KPv,
+    const void* __restrict__ VPv, const int32_t* __restrict__ BT,
     const int32_t* __restrict__ SL, int* __restrict__ wsi,
     float* __restrict__ ws_o, float* __restrict__ ws_l,
     __bf16* __restrict__ O, float* __restrict__ LSE) {
   constexpr int DL = D / 16;  // d columns per lane in the PV step
-  typedef uint32_t vload_t __attribute__((ext_vector_type(DL / 2)));
+  typedef typename std::conditional<KV8, uint8_t, __bf16>::type kv_t;
+  using Regs = PageRegs<D, KV8>;
+  typedef uint32_t vload_t __attribute__((ext_vector_type(DL / 2)));  // DL bf16
+  const kv_t* __restrict__ KP = static_cast<const kv_t*>(KPv);
+  const kv_t* __restrict__ VP = static_cast<const kv_t*>(VPv);
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int row16 = lane >> 4;
@@ -169,29 +215,54 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   };
   // K and V are read exactly once: nontemporal loads stream them past the
   // caches instead of evicting lines other waves still use (-10% time).
-  auto load_page = [&](long base, bf16x8 (&kd)[D / 32], vload_t (&vd)[4]) {
-    const __bf16* kp = KP + base + (long)col * tok_stride + 8 * row16;
+  auto load_page = [&](long base, Regs& pr) {
+    const kv_t* kp = KP + base + (long)col * tok_stride +
+                     (KV8 ? (D / 4) * row16 : 8 * row16);
+    const kv_t* vp = VP + base + (long)(4 * row16) * tok_stride + DL * col;
+    if constexpr (!KV8) {
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      kd[s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kp + 32 * s));
-    const __bf16* vp = VP + base + (long)(4 * row16) * tok_stride + DL * col;
+      for (int s = 0; s < D / 32; ++s)
+        pr.k[s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kp + 32 * s));
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      vd[rr] = __builtin_nontemporal_load(reinterpret_cast<const vload_t*>(vp + rr * tok_stride));
+      for (int rr = 0; rr < 4; ++rr)
+        pr.v[rr] = __builtin_nontemporal_load(
+            reinterpret_cast<const typename Regs::vrow_t*>(vp + rr * tok_stride));
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 64; ++s)
+        pr.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 16 * s));
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        pr.v[rr] = __builtin_nontemporal_load(
+            reinterpret_cast<const typename Regs::vrow_t*>(vp + rr * tok_stride));
+    }
   };
 
   // query heads of the group as the B operand: head col, d = 32s + 8*row16
+  // (e4m3 cache: d = (D/4)*row16 + 8s, the K codes' order)
   bf16x8 qf[D / 32];
   float m, lp;  // exponent reference of head `col`; its partial sum
   float o[GP][DL];
   bool piece_bad;
 
-  auto process = [&](const bf16x8 (&kf)[D / 32], const vload_t (&vv)[4],
-                     bool bad, int page, int lim) {
+  auto process = [&](const Regs& pr_in, bool bad, int page, int lim) {
     piece_bad |= bad;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) acc = mfma_16x16x32_bf16(kf[s], qf[s], acc);
+    for (int s = 0; s < D / 32; ++s) {
+      bf16x8 kf;
+      if constexpr (!KV8) {
+        kf = pr_in.k[s];
+      } else {
+        float f[8];
+        e4m3x4_to_f32(pr_in.k[s / 2][2 * (s & 1)], f);
+        e4m3x4_to_f32(pr_in.k[s / 2][2 * (s & 1) + 1], f + 4);
+        const u32x4 w = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                         pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+        kf = __builtin_bit_cast(bf16x8, w);
+      }
+      acc = mfma_16x16x32_bf16(kf, qf[s], acc);
+    }
     // lane: tokens 4*row16 + v of this page, head col
     const int tok0 = page * kPage + 4 * row16;
 #pragma unroll
@@ -225,18 +296,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       float vf[DL];
+      if constexpr (!KV8) {
 #pragma unroll
-      for (int e = 0; e < DL / 2; ++e) {
-        vf[2 * e] = bf16_lo(vv[rr][e]);
-        vf[2 * e + 1] = bf16_hi(vv[rr][e]);
+        for (int e = 0; e < DL / 2; ++e) {
+          vf[2 * e] = bf16_lo(pr_in.v[rr][e]);
+          vf[2 * e + 1] = bf16_hi(pr_in.v[rr][e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < DL / 4; ++e) e4m3x4_to_f32(pr_in.v[rr][e], vf + 4 * e);
       }
       PvAccumulate<GP, GP, DL>::run(o, pr[rr], vf);
     }
   };
 
   // Pieces: the part of request b inside this range, pages [p, pe).
-  bf16x8 kA[D / 32], kB[D / 32];
-  vload_t vA[4], vB[4];
+  // pages in flight per wave: an e4m3 page is half the bytes, so it keeps
+  // more of them in flight for the same bytes
+  constexpr int NS = KV8 ? kSlots8 : 2;
+  Regs slot_regs[NS];
+  bool slot_bad[NS];
   int b = b0, p = x0 - s0, x = x0;
   for (;;) {
     const int L = clamp_len(SL[b], max_len);
@@ -251,7 +330,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
           Qp + ((long)b * a.Hq + (long)hkv * G + (qv ? col : 0)) * D;
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * row16);
+        const int qd = KV8 ? (D / 4) * row16 + 8 * s : 32 * s + 8 * row16;
+        bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qrow + qd);
         if (!qv) q8 = bf16x8{};
         qf[s] = q8;
       }
@@ -264,28 +344,29 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
       for (int e = 0; e < DL; ++e) o[g][e] = 0.f;
     piece_bad = false;
 
-    // Two page slots, each reloaded right after it is computed. Loads past
-    // the piece repeat its last page (cached, never used); an odd piece
-    // ends with slot B on such a page, fully masked.
-    // The prologue issues Q, slot A, slot B in that order (the barriers pin
-    // it), the same order the loop leaves behind, so the waits at the loop
-    // head count only slot A's loads.
-    bool badA, badB;
+    // NS page slots, each reloaded right after it is computed. Loads past
+    // the piece repeat its last page (cached, never used); the pages a
+    // piece's last round computes past its end are fully masked.
+    // The prologue issues Q, then slots 0, 1, ... in order (the barriers
+    // pin it), the same order the loop leaves behind, so the wait before a
+    // slot is computed counts only that slot's loads.
     __builtin_amdgcn_sched_barrier(0);
-    load_page(page_base(row[p], badA), kA, vA);
-    __builtin_amdgcn_sched_barrier(0);
-    load_page(page_base(row[min(p + 1, pe - 1)], badB), kB, vB);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int q = p; q < pe; q += 2) {
-      const int idA = row[min(q + 2, pe - 1)];
-      const int idB = row[min(q + 3, pe - 1)];
-      process(kA, vA, badA, q, lim);
-      // keep each reload after the last read of its slot
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      load_page(page_base(row[min(p + sl, pe - 1)], slot_bad[sl]), slot_regs[sl]);
       __builtin_amdgcn_sched_barrier(0);
-      load_page(page_base(idA, badA), kA, vA);
-      process(kB, vB, badB, q + 1, lim);
-      __builtin_amdgcn_sched_barrier(0);
-      load_page(page_base(idB, badB), kB, vB);
+    }
+    for (int q = p; q < pe; q += NS) {
+      int ids[NS];
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) ids[sl] = row[min(q + NS + sl, pe - 1)];
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        process(slot_regs[sl], slot_bad[sl], q + sl, lim);
+        // keep each reload after the last read of its slot
+        __builtin_amdgcn_sched_barrier(0);
+        load_page(page_base(ids[sl], slot_bad[sl]), slot_regs[sl]);
+      }
     }
 
     // Emit the piece: final output when it is the whole request, else a
@@ -309,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
       const float mg = lane_value(m, g);
       const float lg = lane_value(ls, g);
       const bool live = lg > 0.f;
-      float inv = live ? 1.f / lg : 0.f;
+      float inv = live ? a.sv / lg : 0.f;
       float lse = live ? (mg + fast_log2(lg)) * kLn2 : kNegInf;
       if (piece_bad) {
         inv = __builtin_nanf("");
@@ -422,28 +503,33 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   if (lane == 0 && LSE != nullptr) LSE[hq] = L_out;
 }
 
-template <int D, int GP, int NW>
+template <int D, int GP, int NW, bool KV8>
 void* kernel_ptr() {
-  return reinterpret_cast<void*>(&decode_kernel<D, GP, NW>);
+  return reinterpret_cast<void*>(&decode_kernel<D, GP, NW, KV8>);
 }
 
-// Kernel instance for head dim d, group size G and waves per workgroup nw.
-void* select_kernel(int d, int G, int nw) {
+// Kernel instance for head dim d, group size G, waves per workgroup nw and
+// the cache's storage (bf16 or e4m3 codes).
+template <bool KV8>
+void* select_kernel_t(int d, int G, int nw) {
 #define FA_PICK8(DD, NWW)                                         \
-  if (G <= 1) return kernel_ptr<DD, 1, NWW>();                    \
-  if (G <= 2) return kernel_ptr<DD, 2, NWW>();                    \
-  if (G <= 4) return kernel_ptr<DD, 4, NWW>();                    \
-  return kernel_ptr<DD, 8, NWW>();
+  if (G <= 1) return kernel_ptr<DD, 1, NWW, KV8>();               \
+  if (G <= 2) return kernel_ptr<DD, 2, NWW, KV8>();               \
+  if (G <= 4) return kernel_ptr<DD, 4, NWW, KV8>();               \
+  return kernel_ptr<DD, 8, NWW, KV8>();
   // eight-wave workgroups are planned only for groups of <= 8 heads
   if (d == 128) {
     if (nw == 8) { FA_PICK8(128, 8) }
-    if (G > 8) return kernel_ptr<128, 16, 4>();
+    if (G > 8) return kernel_ptr<128, 16, 4, KV8>();
     FA_PICK8(128, 4)
   }
   if (nw == 8) { FA_PICK8(64, 8) }
-  if (G > 8) return kernel_ptr<64, 16, 4>();
+  if (G > 8) return kernel_ptr<64, 16, 4, KV8>();
   FA_PICK8(64, 4)
 #undef FA_PICK8
+}
+void* select_kernel(int d, int G, int nw, bool kv8) {
+  return kv8 ? select_kernel_t<true>(d, G, nw) : select_kernel_t<false>(d, G, nw);
 }
 
 // Waves the current device holds at once for this kernel instance.
@@ -479,7 +565,9 @@ bool plan_decode(int B, int Hq, int Hkv, int d, int max_pages, int num_splits,
   if (num_splits > 0) {
     R = num_splits;
   } else {
-    const int waves = resident_waves(select_kernel(d, G, nw), nw);
+    // sized by the bf16 instance for both storages, so one workspace query
+    // serves both entry points
+    const int waves = resident_waves(select_kernel(d, G, nw, false), nw);
     R = waves / Hkv;
   }
   R = ((R + p->waves_per_head - 1) / p->waves_per_head) * p->waves_per_head;
@@ -505,10 +593,11 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p) {
   k.ngroups = p.head_groups;
   k.max_pages = a.max_pages;
   k.R = p.ranges;
-  k.c = a.scale * kLog2e;
+  k.c = a.scale * kLog2e * (a.kv_fp8 ? a.s_k : 1.f);
+  k.sv = a.kv_fp8 ? a.s_v : 1.f;
   const __bf16* q = static_cast<const __bf16*>(a.q);
-  const __bf16* kp = static_cast<const __bf16*>(a.k_pool);
-  const __bf16* vp = static_cast<const __bf16*>(a.v_pool);
+  const void* kp = a.k_pool;
+  const void* vp = a.v_pool;
   const int32_t* bt = a.block_table;
   const int32_t* sl = a.seq_lens;
   int* wsi = static_cast<int*>(a.ws);
@@ -516,7 +605,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p) {
   float* ws_l = static_cast<float*>(a.ws) + p.off_l;
   __bf16* o = static_cast<__bf16*>(a.o);
   float* lse = a.lse;
-  void* fn = select_kernel(a.d, k.G, p.nw);
+  void* fn = select_kernel(a.d, k.G, p.nw, a.kv_fp8);
   void* args[] = {&k, &q, &kp, &vp, &bt, &sl, &wsi, &ws_o, &ws_l, &o, &lse};
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.grid),
                                  dim3((unsigned)(p.nw * 64)), args, 0,

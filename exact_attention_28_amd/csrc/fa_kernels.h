@@ -55,6 +55,8 @@ struct DecodeArgs {
   void* o;
   float* lse;  // may be null
   void* ws;    // page-range bookkeeping and partials
+  bool kv_fp8;     // pools hold e4m3 codes with per-tensor scales
+  float s_k, s_v;  // the pools' scales (1 for bf16)
   hipStream_t stream;
 };
 

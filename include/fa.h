@@ -10,6 +10,8 @@
  *                    LSE, with P re-computed on chip (never stored).
  *   fa_paged_decode  one query token per request against a paged KV cache,
  *                    split over workgroups and merged by log-sum-exp.
+ *   fa_paged_decode_fp8kv  the same over a cache stored as e4m3 codes with
+ *                    per-tensor scales (half the bytes to read).
  *
  * Sources (cited by page and section):
  *   [FA3-guide]  "Flash Attention 3 指南：GPU IO 优化的终极武器"
@@ -215,6 +217,31 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                     int d, int max_pages_per_seq, float scale, void* o,
                     float* lse, void* workspace, size_t workspace_bytes,
                     int num_splits, void* stream);
+
+/*
+ * fa_paged_decode_fp8kv - fa_paged_decode over a KV cache stored as OCP
+ * e4m3 codes with one fp32 scale per pool: the cached values are
+ * K = code_k * s_k and V = code_v * s_v (the per-tensor scaling of the
+ * [FA3-guide] fp8 listing applied to the paged cache of [FA3-paged §3.2]).
+ * The query stays bf16 and the result is exact attention over those
+ * values: the codes are widened exactly in registers, s_k is folded into
+ * the score scale and s_v into the final normalisation.
+ *
+ * Arguments as fa_paged_decode, except:
+ * k_pool,
+ * v_pool       [num_pages, page_size, Hkv, d] e4m3 codes (one byte each)
+ * kv_descale   HOST pointer to two floats (s_k, s_v), finite and > 0;
+ *              NULL or a bad value -> FA_EDESCALE. Read during the call.
+ * workspace    sized by fa_paged_decode_workspace_size (the same plan).
+ */
+int fa_paged_decode_fp8kv(const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, int page_size,
+                          int num_pages, int B, int Hq, int Hkv, int d,
+                          int max_pages_per_seq, float scale,
+                          const float* kv_descale, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          int num_splits, void* stream);
 
 /* fa_strerror - static, NUL-terminated description of a return code. */
 const char* fa_strerror(int code);

@@ -11,6 +11,7 @@ from .attention import (  # noqa: F401
     merge_partials,
     online_softmax_stats,
     paged_decode,
+    paged_decode_fp8,
     safe_softmax,
     softmax_stats,
 )

@@ -67,6 +67,7 @@ __all__ = [
     "merge_partials",
     "gather_paged_kv",
     "paged_decode",
+    "paged_decode_fp8",
     "attention_backward",
 ]
 
@@ -265,6 +266,17 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, page_size, scale):
         out[b] = o[0, :, 0, :]
         lse[b] = s[0, :, 0]
     return out, lse
+
+
+def paged_decode_fp8(q, k_codes, v_codes, s_k, s_v, block_table, seq_lens,
+                     page_size, scale):
+    """Paged decode over a cache stored as e4m3 codes with per-pool scales
+    ([FA3-guide] fp8 listing's per-tensor scaling, [FA3-paged §3.2] pages):
+    the cached values are code * s, multiplied out exactly in fp64, then
+    ``paged_decode`` of those values."""
+    kx = np.asarray(k_codes, dtype=np.float64) * float(s_k)
+    vx = np.asarray(v_codes, dtype=np.float64) * float(s_v)
+    return paged_decode(q, kx, vx, block_table, seq_lens, page_size, scale)
 
 
 # --------------------------------------------------------------------------

@@ -214,3 +214,27 @@ def test_workspace_size(lib):
     assert ws(0, 4, 1, 64, 10, 16, 0) == 0
     assert ws(1, 4, 1, 64, 10, 8, 0) == 0
     assert ws(1, 4, 1, 64, 10, 16, 70000) == 0        # above the range cap
+
+
+def dec8(**kw):
+    a = dict(q=P, k_pool=P, v_pool=P, block_table=P, seq_lens=P, page_size=16,
+             num_pages=100, B=4, Hq=32, Hkv=8, d=128, max_pages_per_seq=512,
+             scale=0.1, kv_descale=(0.01, 0.02), o=P, lse=P, workspace=P,
+             workspace_bytes=1 << 40, num_splits=0, stream=None)
+    a.update(kw)
+    return fa.fa_paged_decode_fp8kv(**a, check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_descale=None), L.FA_EDESCALE),
+    (dict(kv_descale=(0.0, 1.0)), L.FA_EDESCALE),
+    (dict(kv_descale=(1.0, -2.0)), L.FA_EDESCALE),
+    (dict(kv_descale=(float("inf"), 1.0)), L.FA_EDESCALE),
+    (dict(q=None), L.FA_EINVAL_NULL),
+    (dict(d=96), L.FA_EUNSUPPORTED_D),
+    (dict(page_size=8), L.FA_EPAGE),
+    (dict(workspace_bytes=8), L.FA_EWORKSPACE),
+    (dict(v_pool=P + 8), L.FA_EALIGN),
+])
+def test_decode_fp8kv_rejects(lib, kw, code):
+    assert dec8(**kw) == code

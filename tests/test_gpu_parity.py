@@ -213,6 +213,35 @@ def _gpu_decode(fa, di, num_splits=0, num_pages=None):
     return out.double().cpu().numpy(), lse.double().cpu().numpy()
 
 
+def _gpu_decode_fp8(fa, di, num_splits=0):
+    dev = torch.device("cuda:0")
+    q = di.q.to(dev)
+    kp, vp = di.k_pool.to(dev), di.v_pool.to(dev)
+    bt, sl = di.block_table.to(dev), di.seq_lens.to(dev)
+    B, Hq, d = q.shape
+    npg, page, Hkv, _ = kp.shape
+    maxp = bt.shape[1]
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16,
+                     device=dev)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev)
+    need = fa.fa_paged_decode_workspace_size(B, Hq, Hkv, d, maxp, page,
+                                             num_splits)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=dev)
+    fa.fa_paged_decode_fp8kv(q, kp, vp, bt, sl, page, npg, B, Hq, Hkv, d,
+                             maxp, di.scale, di.kv_descale, out, lse, ws,
+                             ws.numel(), num_splits)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def _oracle_decode_fp8(di):
+    return oracle.paged_decode_fp8(W.as_f64(di.q), W.as_f64(di.k_pool),
+                                   W.as_f64(di.v_pool), *di.kv_descale,
+                                   di.block_table.numpy(),
+                                   di.seq_lens.numpy(), di.page_size,
+                                   di.scale)
+
+
 def _oracle_decode(di):
     return oracle.paged_decode(W.as_f64(di.q), W.as_f64(di.k_pool),
                                W.as_f64(di.v_pool), di.block_table.numpy(),
@@ -301,3 +330,27 @@ def test_decode_full_workload(fa):
     o, lse = _gpu_decode(fa, di)
     ro, rl = _oracle_decode(di)
     _compare(o, lse, ro, rl, "bf16", name)
+
+
+# ------------------------------------------------------ decode, e4m3 cache
+# The codes are widened exactly and the query stays bf16, so the bars are
+# the bf16 decode's, against the oracle on the dequantised cache.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (16, 1), (6, 2)])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_decode_fp8_cache_sweep(fa, d, hq, hkv, num_splits):
+    lens = [0, 1, 15, 16, 17, 31, 33, 100, 255, 256, 257, 1000]
+    di = W.decode_inputs(len(lens), hq, hkv, d, lens=lens, max_pages=80,
+                         seed=d + hq + 1, extra_pages=5, kv_dtype="fp8")
+    o, lse = _gpu_decode_fp8(fa, di, num_splits)
+    ro, rl = _oracle_decode_fp8(di)
+    _compare(o, lse, ro, rl, "bf16",
+             f"fp8-cache decode d{d} {hq}/{hkv} splits={num_splits}")
+
+
+def test_decode_fp8_cache_full_workload(fa):
+    name = next(iter(W.DECODE_CONFIGS))
+    di = W.decode_config(name, kv_dtype="fp8")
+    o, lse = _gpu_decode_fp8(fa, di)
+    ro, rl = _oracle_decode_fp8(di)
+    _compare(o, lse, ro, rl, "bf16", name + " e4m3 cache")

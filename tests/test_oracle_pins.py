@@ -455,6 +455,37 @@ def test_fp8_dequantisation_and_scales():
     assert np.max(np.abs(o4 - o)) < 1e-13
 
 
+def test_paged_decode_fp8_cache_scales():
+    # an e4m3 cache: codes times one scale per pool; the decode of those
+    # values is the plain paged decode of the dequantised pools, only
+    # scale * s_k matters for the scores and O is linear in s_v
+    rng = np.random.default_rng(19)
+    vals = np.array([-448, -7.5, -1, -0.125, 0, 0.25, 1.75, 3, 64, 448.0])
+    n_pages, page, Hkv, d = 6, 4, 2, 3
+    kc = rng.choice(vals, (n_pages, page, Hkv, d))
+    vc = rng.choice(vals, (n_pages, page, Hkv, d))
+    q = rng.standard_normal((2, 4, d))
+    table = np.array([[3, 0, 5], [1, 4, -1]])
+    lens = np.array([10, 6])
+    sk, sv = 0.0031, 0.0087
+    o, lse = oracle.paged_decode_fp8(q, kc, vc, sk, sv, table, lens, page, 0.6)
+    # the dequantised pools by hand, gathered request by request
+    for r in range(2):
+        n = -(-lens[r] // page)
+        K = np.concatenate([kc[table[r, p]] for p in range(n)])[: lens[r]] * sk
+        V = np.concatenate([vc[table[r, p]] for p in range(n)])[: lens[r]] * sv
+        for h in range(4):
+            hk = h // 2
+            sc = 0.6 * (K[:, hk, :] @ q[r, h])
+            w = np.exp(sc - sc.max())
+            assert abs(np.log(w.sum()) + sc.max() - lse[r, h]) < 1e-12
+            assert np.max(np.abs((w / w.sum()) @ V[:, hk, :] - o[r, h])) < 1e-12
+    o2, l2 = oracle.paged_decode_fp8(q, kc, vc, 1.0, 2 * sv, table, lens,
+                                     page, 0.6 * sk)
+    assert np.max(np.abs(o2 - 2 * o)) < 1e-12
+    assert np.max(np.abs(l2 - lse)) < 1e-12
+
+
 # ---------------------------------------------------------------- backward
 # The gradient of the definition is pinned by numerical differentiation of
 # the forward oracle (central differences in fp64 on tiny inputs, an

@@ -115,3 +115,22 @@ def test_decode_inputs_structure():
 def test_config_table(name):
     c = W.PREFILL_CONFIGS[name]
     assert c["Hq"] % c["Hkv"] == 0 and c["d"] in (64, 128)
+
+
+def test_decode_inputs_fp8_cache():
+    bf = W.decode_inputs(3, 8, 2, 64, lens=[5, 33, 0], max_pages=4, seed=3)
+    di = W.decode_inputs(3, 8, 2, 64, lens=[5, 33, 0], max_pages=4, seed=3,
+                         kv_dtype="fp8")
+    assert di.k_pool.dtype == torch.float8_e4m3fn
+    assert di.v_pool.dtype == torch.float8_e4m3fn
+    s_k, s_v = di.kv_descale
+    assert s_k > 0 and s_v > 0
+    # same draws, same tables and query as the bf16 cache
+    assert torch.equal(di.block_table, bf.block_table)
+    assert torch.equal(di.q, bf.q)
+    # poison slots hold the largest finite code
+    t = int(di.block_table[0, 0])
+    assert torch.all(di.k_pool[t, 5:].float().abs() == W.E4M3_MAX)
+    # real tokens: code * scale within e4m3 rounding of the drawn values
+    k_real = di.k_pool[t, :5].float() * s_k
+    assert torch.max(torch.abs(k_real - bf.k_pool[t, :5].float())) < 0.2

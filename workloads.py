@@ -105,6 +105,7 @@ class DecodeInputs:
     seq_lens: torch.Tensor     # [B] int32
     page_size: int
     scale: float
+    kv_descale: tuple | None = None   # (s_k, s_v) for an e4m3 cache
 
 
 POISON = 1.0e4   # finite filler for token slots past a request's length
@@ -112,7 +113,7 @@ POISON = 1.0e4   # finite filler for token slots past a request's length
 
 def decode_inputs(n_req, Hq, Hkv, d, page_size=16, len_min=512,
                   len_max=8192, seed=42, max_pages=None, lens=None,
-                  extra_pages=0) -> DecodeInputs:
+                  extra_pages=0, kv_dtype="bf16") -> DecodeInputs:
     """A paged KV cache for n_req requests, one query token each.
 
     Draw order: lengths ~ U{len_min..len_max} (unless ``lens`` is given),
@@ -121,6 +122,10 @@ def decode_inputs(n_req, Hq, Hkv, d, page_size=16, len_min=512,
     physical slot given by a seeded permutation of all pages. Slots of the
     last page beyond the request's length hold +/-1e4 so any masking error
     is gross. ``extra_pages`` adds never-referenced pages (also poisoned).
+
+    kv_dtype "fp8": the pools are stored as e4m3 codes with one fp32 scale
+    per pool (amax / 448 of the drawn values), and the poison is the
+    largest finite code (+/-448): finite, so 0 * poison stays 0.
     """
     rng = np.random.default_rng(seed)
     if lens is None:
@@ -135,6 +140,19 @@ def decode_inputs(n_req, Hq, Hkv, d, page_size=16, len_min=512,
     kp = rng.standard_normal((total, page_size, Hkv, d), dtype=np.float32)
     vp = rng.standard_normal((total, page_size, Hkv, d), dtype=np.float32)
     perm = rng.permutation(total)
+    poison = POISON
+    kv_descale = None
+    if kv_dtype == "fp8":
+        scales = []
+        for pool in (kp, vp):
+            amax = float(np.max(np.abs(pool))) if pool.size else 0.0
+            sc = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+            pool /= sc                      # now in code units
+            scales.append(float(sc))
+        kv_descale = tuple(scales)
+        poison = E4M3_MAX
+    elif kv_dtype != "bf16":
+        raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
     table = np.full((n_req, max_pages), -1, dtype=np.int32)
     slot = 0
     for r in range(n_req):
@@ -146,27 +164,35 @@ def decode_inputs(n_req, Hq, Hkv, d, page_size=16, len_min=512,
             phys = table[r, n_pages[r] - 1]
             sign = rng.choice(np.array([-1.0, 1.0], dtype=np.float32),
                               size=(page_size - tail, Hkv, d))
-            kp[phys, tail:] = POISON * sign
-            vp[phys, tail:] = -POISON * sign
+            kp[phys, tail:] = poison * sign
+            vp[phys, tail:] = -poison * sign
     for p in perm[slot:]:                      # unreferenced pages
-        kp[p] = POISON
-        vp[p] = -POISON
+        kp[p] = poison
+        vp[p] = -poison
+    if kv_dtype == "fp8":
+        def store(x):
+            t = torch.from_numpy(x)
+            return torch.clamp(t, -E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    else:
+        def store(x):
+            return torch.from_numpy(x).to(torch.bfloat16)
     return DecodeInputs(
         q=torch.from_numpy(q).to(torch.bfloat16),
-        k_pool=torch.from_numpy(kp).to(torch.bfloat16),
-        v_pool=torch.from_numpy(vp).to(torch.bfloat16),
+        k_pool=store(kp),
+        v_pool=store(vp),
         block_table=torch.from_numpy(table),
         seq_lens=torch.from_numpy(lens.astype(np.int32)),
         page_size=int(page_size),
         scale=1.0 / math.sqrt(d),
+        kv_descale=kv_descale,
     )
 
 
-def decode_config(name, seed=42) -> DecodeInputs:
+def decode_config(name, seed=42, kv_dtype="bf16") -> DecodeInputs:
     c = DECODE_CONFIGS[name]
     return decode_inputs(c["n_req"], c["Hq"], c["Hkv"], c["d"],
                          page_size=c["page_size"], len_min=c["len_min"],
-                         len_max=c["len_max"], seed=seed)
+                         len_max=c["len_max"], seed=seed, kv_dtype=kv_dtype)
 
 
 def as_f64(t: torch.Tensor) -> np.ndarray:
