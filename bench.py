@@ -9,11 +9,13 @@ One step = one pass of the whole path over its synthetic workloads:
   4. the backward of workload 1 (fa_bwd: dQ, dK, dV from O, LSE and a
      seeded dO)
   5. workload 2 over a cache stored as e4m3 codes (fa_paged_decode_fp8kv)
+  6. the non-causal bf16 prefill B=4, H=16, N=2048, d=128, fused (fa_fwd)
+     and as the pages' three-kernel contrast (fa_naive_attention)
 Inputs are seeded N(0,1) draws (seed 42) already resident in HBM when the
 timed region starts. Each launch is bracketed by HIP events on the stream
 it runs on; the step time is the wall time of K steps of legs 1-3 between
-two device synchronisations. Legs 4 and 5 are timed afterwards, K
-launches each.
+two device synchronisations. Legs 4-6 are timed afterwards, K launches
+each.
 
 Prints ONE JSON line. `value` is the bf16 causal prefill throughput in
 TFLOPS (algorithmic FLOPs: 4*d per visible (query, key) pair per query
@@ -42,6 +44,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 PREFILL = "bf16_causal_gqa_b1_hq32_hkv8_n16384_d128"
+NONCAUSAL = "bf16_b4_h16_n2048_d128"
 FP8 = "fp8_b2_h16_n8192_d128"
 DECODE = "paged_decode_r64_hq32_hkv8_d128_p16"
 
@@ -146,7 +149,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,fp8,bwd,decode8",
+    ap.add_argument("--legs",
+                    default="prefill,decode,fp8,bwd,decode8,noncausal,naive",
                     help="comma list of legs to run (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -252,6 +256,27 @@ def main():
             d8.scale, d8.kv_descale, od8, ld8, ws8, ws8.numel(), 0, stream)
         info["decode8"] = dict(bytes=decode_bytes(d8, Hkv8, dd8, 1),
                                kv_tokens=int(d8.seq_lens.sum()))
+    if "noncausal" in legs or "naive" in legs:
+        # the non-causal bf16 prefill, fused and as the pages' three-kernel
+        # contrast (S and P through HBM)
+        cn = W.PREFILL_CONFIGS[NONCAUSAL]
+        i_n = W.prefill_config(NONCAUSAL)
+        qn, kn, vn = (t.to(dev) for t in (i_n.q, i_n.k, i_n.v))
+        on = torch.empty(qn.shape, dtype=torch.bfloat16, device=dev)
+        ln = torch.empty(qn.shape[:3], dtype=torch.float32, device=dev)
+        args_n = (cn["B"], cn["Hq"], cn["Hkv"], cn["Nq"], cn["Nk"], cn["d"],
+                  i_n.scale, False)
+        if "noncausal" in legs:
+            calls["noncausal"] = lambda: fa.fa_fwd(
+                qn, kn, vn, on, ln, *args_n, fa.FA_DTYPE_BF16, None, stream)
+            info["noncausal"] = dict(flops=prefill_flops(cn), cfg=cn)
+        if "naive" in legs:
+            wsn = torch.empty(fa.fa_naive_workspace_size(
+                cn["B"], cn["Hq"], cn["Nq"], cn["Nk"]), dtype=torch.uint8,
+                device=dev)
+            calls["naive"] = lambda: fa.fa_naive_attention(
+                qn, kn, vn, on, ln, *args_n, wsn, wsn.numel(), stream)
+            info["naive"] = dict(flops=prefill_flops(cn), cfg=cn)
     torch.cuda.synchronize()
     print(f"bench: inputs resident, legs={legs}", file=sys.stderr, flush=True)
 
@@ -259,7 +284,7 @@ def main():
     # leg is timed after it in a phase of its own, so its heat and power
     # draw do not change the clocks the forward legs run at
     order = [x for x in ("prefill", "decode", "fp8", "copy") if x in calls]
-    extra = [x for x in ("bwd", "decode8") if x in calls]
+    extra = [x for x in ("bwd", "decode8", "noncausal", "naive") if x in calls]
 
     def timed(names, steps):
         ev = {n: [] for n in names}
@@ -374,6 +399,28 @@ def main():
         workload.append("paged decode over an e4m3 cache (same requests)")
         if "value" not in out:
             out["value"], out["unit"] = gbs, "GB/s"
+    for leg in ("noncausal", "naive"):
+        if leg not in order:
+            continue
+        c = info[leg]["cfg"]
+        t = statistics.mean(ms[leg]) / 1e3
+        tf = info[leg]["flops"] / t / 1e12
+        heads = c["B"] * c["Hq"]
+        N, d = c["Nq"], c["d"]
+        entry = {"value": tf, "unit": "TFLOPS", "launch_ms_mean": t * 1e3,
+                 "launch_ms_min": min(ms[leg])}
+        if leg == "naive":
+            # the pages' traffic ledger, 8Nd + 8N^2 bytes per head
+            entry["ledger_bytes"] = heads * (8 * N * d + 8 * N * N)
+            entry["ledger_GB/s"] = entry["ledger_bytes"] / t / 1e9
+            entry["kernels"] = ("naive_scores_kernel + naive_softmax_kernel"
+                                " + naive_pv_kernel")
+        else:
+            entry["ledger_bytes"] = heads * 8 * N * d
+        out["bf16_noncausal_" + leg if leg == "naive" else
+            "bf16_noncausal_fused"] = entry
+        workload.append(f"bf16 prefill B={c['B']} H={c['Hq']} N={N} d={d} "
+                        f"({'three-kernel contrast' if leg == 'naive' else 'fused'})")
     if "copy" in order:
         t = statistics.mean(ms["copy"]) / 1e3
         out["copy_calibration"] = {"bytes_per_launch": info["copy"]["bytes"],

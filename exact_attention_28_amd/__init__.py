@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     fa_bwd,
     fa_bwd_workspace_size,
     fa_fwd,
+    fa_naive_attention,
+    fa_naive_workspace_size,
     fa_paged_decode,
     fa_paged_decode_fp8kv,
     fa_paged_decode_workspace_size,

@@ -31,7 +31,8 @@ FA_ESPLITS = -10
 FA_EALIGN = -11
 
 # every function include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_naive_attention",
+           "fa_naive_workspace_size", "fa_paged_decode",
            "fa_paged_decode_fp8kv", "fa_paged_decode_workspace_size",
            "fa_strerror")
 
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH):
     lib.fa_paged_decode.restype = i
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                     f, vp, vp, vp, sz, i, vp]
+    lib.fa_naive_attention.restype = i
+    lib.fa_naive_attention.argtypes = [vp] * 5 + [i] * 6 + [f, i, vp, sz, vp]
+    lib.fa_naive_workspace_size.restype = sz
+    lib.fa_naive_workspace_size.argtypes = [i, i, i, i]
     lib.fa_paged_decode_fp8kv.restype = i
     lib.fa_paged_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i,
                                           i, i, f, vp, vp, vp, vp, sz, i, vp]
@@ -186,6 +191,24 @@ def fa_paged_decode_fp8kv(q, k_pool, v_pool, block_table, seq_lens,
         ctypes.cast(desc, ctypes.c_void_p) if desc else None, _ptr(o),
         _ptr(lse), _ptr(workspace), int(workspace_bytes), int(num_splits),
         _stream(stream, q, o))
+    if check:
+        _check(code)
+    return code
+
+
+def fa_naive_workspace_size(B, Hq, Nq, Nk) -> int:
+    return int(load_library().fa_naive_workspace_size(int(B), int(Hq),
+                                                      int(Nq), int(Nk)))
+
+
+def fa_naive_attention(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                       workspace, workspace_bytes, stream=None,
+                       check=True) -> int:
+    """The three-kernel contrast path (see include/fa.h)."""
+    code = load_library().fa_naive_attention(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq),
+        int(Hkv), int(Nq), int(Nk), int(d), float(scale), int(bool(causal)),
+        _ptr(workspace), int(workspace_bytes), _stream(stream, q, o))
     if check:
         _check(code)
     return code

@@ -173,6 +173,51 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
   return (int)fa::launch_bwd_bf16(a);
 }
 
+size_t fa_naive_workspace_size(int B, int Hq, int Nq, int Nk) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || Nk <= 0) return 0;
+  if (numel4(B, Hq, Nq, Nk) < 0 || numel4(B, Hq, Nq, Nk) > INT64_MAX / 4) return 0;
+  return fa::naive_workspace_bytes(B, Hq, Nq, Nk);
+}
+
+int fa_naive_attention(const void* q, const void* k, const void* v, void* o,
+                       float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                       int d, float scale, int causal, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o) return FA_EINVAL_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return FA_EINVAL_DIM;
+  if (d != 64 && d != 128) return FA_EUNSUPPORTED_D;
+  if (Hq % Hkv != 0) return FA_EGQA;
+  if (!(isfinite(scale) && scale > 0.f)) return FA_ESCALE;
+  if (Nk % 8 != 0 || Nk > 16384) return FA_EINVAL_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      ((uintptr_t)lse & 3u) != 0)
+    return FA_EALIGN;
+  if ((long)Nq * d > kMaxIndex || (long)Nk * d > kMaxIndex) return FA_EINVAL_DIM;
+  if (numel4(B, Hq, Nq, d) < 0 || numel4(B, Hkv, Nk, d) < 0) return FA_EINVAL_DIM;
+  if ((long)B * Hq * Nq > kMaxIndex) return FA_EINVAL_DIM;
+  const size_t need = fa_naive_workspace_size(B, Hq, Nq, Nk);
+  if (need == 0) return FA_EINVAL_DIM;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return FA_EWORKSPACE;
+  fa::NaiveArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.ws = workspace;
+  a.stream = static_cast<hipStream_t>(stream);
+  return (int)fa::launch_naive_bf16(a);
+}
+
 static int decode_check(int B, int Hq, int Hkv, int d, int max_pages,
                         int page_size, int num_splits) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_pages <= 0) return FA_EINVAL_DIM;

@@ -40,6 +40,21 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int B, int Hq, int Nq);
 hipError_t launch_bwd_bf16(const BwdArgs& a);
 
+struct NaiveArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  bool causal;
+  void* ws;  // S (fp16), then P (bf16) in place: B*Hq*Nq*Nk * 2 bytes
+  hipStream_t stream;
+};
+size_t naive_workspace_bytes(int B, int Hq, int Nq, int Nk);
+hipError_t launch_naive_bf16(const NaiveArgs& a);
+
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_fp8(const FwdArgs& a);

@@ -1,0 +1,309 @@
+// fa_naive.hip - the three-kernel attention the pages use as the contrast
+// to the fused kernel ([Capstone §0] and §1.1): the score matrix S and the
+// probabilities P are materialised in device memory, every kernel a round
+// trip through HBM:
+//   naive_scores_kernel   S = scale * Q K^T          (write S: 2 bytes/score)
+//   naive_softmax_kernel  P = softmax(S) row by row  (read S, write P)
+//   naive_pv_kernel       O = P V                    (read P and V, write O)
+// which moves 8Nd + 8N^2 bytes per head at 2 bytes per element ([Capstone
+// §1.1], the traffic ledger) against the fused kernel's 8Nd. S is stored as
+// fp16 (the pages' element type, which keeps the scores' precision) and P
+// as bf16 (the PV operand type) in the same buffer, each row of P written
+// over its row of S. The masking (bottom-right causal) is applied in the
+// softmax kernel, as a plain implementation would; the product kernels do
+// not skip masked tiles.
+//
+// The two products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation
+// (Q K^T with K tiles staged in LDS; P V with V tiles staged in LDS and read
+// transposed); they are written to be reasonable, not slow, so that what the
+// measurement shows is the traffic.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
+                                   16, 0, 0);
+}
+
+// 64-row tile of D bf16 in LDS, 1 KB blocks at a 1040 B pitch, row r in
+// block r % NB, slot r / NB (16-byte row reads conflict free).
+template <int D>
+struct Tile64 {
+  static constexpr int RPB = 1024 / (2 * D);
+  static constexpr int NB = 64 / RPB;
+  static constexpr int CPR = D / 8;
+  static constexpr int PITCH = 1040;
+  static constexpr int BYTES = NB * PITCH;
+  static constexpr int BPW = NB / 4;
+  static __device__ __forceinline__ int row_off(int r) {
+    return (r % NB) * PITCH + (r / NB) * (2 * D);
+  }
+};
+template <int D>
+__device__ __forceinline__ void load64(const __bf16* src, int r0, int n,
+                                       lds_char* dst, int w, int lane) {
+  using T = Tile64<D>;
+  const int slot = lane / T::CPR, chunk = lane % T::CPR;
+#pragma unroll
+  for (int i = 0; i < T::BPW; ++i) {
+    const int b = w + 4 * i;
+    const int r = min(r0 + b + T::NB * slot, n - 1);
+    g2lds_16B(src + (long)r * D + 8 * chunk, dst + b * T::PITCH);
+  }
+}
+
+// ----------------------------------------------------------- S = Q K^T
+// Workgroup: 128 query rows (32 per wave) of one (batch, head) against
+// every key, 64 keys per tile. S = Q K^T with Q as the A operand (rows in
+// registers) and K^T as the B operand (key rows from LDS), so a lane holds
+// one key column and consecutive lanes write consecutive keys of a row.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void naive_scores_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+    _Float16* __restrict__ S, int B, int Hq, int Hkv, int Nq, int Nk,
+    float scale) {
+  using T = Tile64<D>;
+  __shared__ __attribute__((aligned(16))) char kl0[T::BYTES];
+  __shared__ __attribute__((aligned(16))) char kl1[T::BYTES];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int n_qt = (Nq + 127) / 128;
+  const TileIdx ti = map_tile(blockIdx.x, n_qt, Hq, Hkv, B, false);
+  const int hk = ti.hq / (Hq / Hkv);
+  const long bh = (long)ti.b * Hq + ti.hq;
+  const __bf16* Kh = K + ((long)ti.b * Hkv + hk) * Nk * D;
+  const int row0 = ti.qt * 128 + 32 * w;
+  const int rowc = min(row0 + r32, Nq - 1);
+  bf16x8 qa[D / 16];  // A operand: row r32, d = 16s + 8h
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    qa[s] = *reinterpret_cast<const bf16x8*>(Q + (bh * Nq + rowc) * D + 16 * s + 8 * h);
+  const int nt = (Nk + 63) / 64;
+  const int kfrag = T::row_off(r32) + 16 * h;
+  auto buf = [&](int i) -> lds_char* { return (lds_char*)(i ? kl1 : kl0); };
+  load64<D>(Kh, 0, Nk, buf(0), w, lane);
+  for (int t = 0; t < nt; ++t) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (t + 1 < nt) load64<D>(Kh, 64 * (t + 1), Nk, buf((t + 1) & 1), w, lane);
+    const lds_char* kp = buf(t & 1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 acc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        acc = mfma_32x32x16_bf16(
+            qa[s], *(const lds_bf16x8*)(kp + kfrag + T::row_off(32 * kb) + 32 * s), acc);
+      // lane: key 64t + 32kb + r32, rows 8(v/4) + 4h + v%4 of the wave's 32
+      const int key = 64 * t + 32 * kb + r32;
+      if (key < Nk) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = row0 + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (row < Nq) S[(bh * Nq + row) * Nk + key] = (_Float16)(acc[v] * scale);
+        }
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------- P = softmax(S)
+// One workgroup per row: the row's scores are read once into registers
+// (NV per thread), the three passes of the safe softmax ([Capstone §2.1])
+// run on them with workgroup reductions, and P (bf16) is written over the
+// row, with the row's LSE. Bottom-right causal mask: key j visible to row
+// i iff j <= i + Nk - Nq.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void naive_softmax_kernel(
+    _Float16* __restrict__ S, float* __restrict__ LSE, int Nq, int Nk,
+    bool causal) {
+  __shared__ float red[kThreads / 64];
+  const long rowid = blockIdx.x;  // (b * Hq + h) * Nq + i
+  const int i = (int)(rowid % Nq);
+  const int lim = causal ? min(Nk, i + (Nk - Nq) + 1) : Nk;  // visible keys
+  _Float16* srow = S + rowid * Nk;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float x[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int j = tid + kThreads * e;
+    x[e] = (j < lim) ? (float)srow[j] : kNegInf;
+  }
+  auto block_reduce = [&](float v, bool is_max) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float u = __shfl_xor(v, o, 64);
+      v = is_max ? fmaxf(v, u) : v + u;
+    }
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int k = 1; k < kThreads / 64; ++k) r = is_max ? fmaxf(r, red[k]) : r + red[k];
+    return r;
+  };
+  float m = kNegInf;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) m = fmaxf(m, x[e]);
+  m = block_reduce(m, true);
+  const float mref = (m == kNegInf) ? 0.f : m;
+  float l = 0.f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    x[e] = fast_exp2((x[e] - mref) * kLog2e);
+    l += x[e];
+  }
+  l = block_reduce(l, false);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  __bf16* prow = reinterpret_cast<__bf16*>(srow);
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int j = tid + kThreads * e;
+    if (j < Nk) prow[j] = (__bf16)(x[e] * inv);
+  }
+  if (tid == 0 && LSE != nullptr) LSE[rowid] = l > 0.f ? m + __logf(l) : kNegInf;
+}
+
+// ----------------------------------------------------------- O = P V
+// Workgroup: 128 rows (32 per wave) of one (batch, head); V streams through
+// LDS in 64-key tiles and is read transposed (ds_read_b64_tr_b16) as the A
+// operand of O^T = V^T P^T; P^T's B operand comes straight from the P rows
+// in HBM (lane: row r32, keys 16j + 4h + 0..3 and + 8, the order the
+// transposed V read delivers).
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void naive_pv_kernel(
+    const __bf16* __restrict__ P, const __bf16* __restrict__ V,
+    __bf16* __restrict__ O, int B, int Hq, int Hkv, int Nq, int Nk) {
+  using T = Tile64<D>;
+  __shared__ __attribute__((aligned(16))) char vl0[T::BYTES];
+  __shared__ __attribute__((aligned(16))) char vl1[T::BYTES];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int h = lane >> 5, r32 = lane & 31, i16 = lane & 15;
+  const int n_qt = (Nq + 127) / 128;
+  const TileIdx ti = map_tile(blockIdx.x, n_qt, Hq, Hkv, B, false);
+  const int hk = ti.hq / (Hq / Hkv);
+  const long bh = (long)ti.b * Hq + ti.hq;
+  const __bf16* Vh = V + ((long)ti.b * Hkv + hk) * Nk * D;
+  const int row = ti.qt * 128 + 32 * w + r32;
+  const int rowc = min(row, Nq - 1);
+  const __bf16* prow = P + (bh * Nq + rowc) * Nk;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
+  // transposed read offsets: rows 16j + 8e + 4h + i16/4 of the tile,
+  // columns 2*(16*((lane>>4)&1) + 4*(i16&3)) bytes (+64 per 32 columns)
+  const int tbase = T::row_off(4 * h + (i16 >> 2)) +
+                    2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3));
+  auto buf = [&](int i) -> lds_char* { return (lds_char*)(i ? vl1 : vl0); };
+  const int nt = (Nk + 63) / 64;
+  load64<D>(Vh, 0, Nk, buf(0), w, lane);
+  for (int t = 0; t < nt; ++t) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (t + 1 < nt) load64<D>(Vh, 64 * (t + 1), Nk, buf((t + 1) & 1), w, lane);
+    const lds_char* vp = buf(t & 1);
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {  // 16-key steps of the tile
+      const int k0 = 64 * t + 16 * j4 + 4 * h;
+      u32x2 lo = {0u, 0u}, hi = {0u, 0u};
+      if (k0 + 4 <= Nk) lo = *reinterpret_cast<const u32x2*>(prow + k0);
+      else
+        for (int e = 0; e < 4; ++e)
+          if (k0 + e < Nk) {
+            const uint16_t bits = reinterpret_cast<const uint16_t*>(prow)[k0 + e];
+            lo[e / 2] |= (uint32_t)bits << (16 * (e & 1));
+          }
+      if (k0 + 12 <= Nk) hi = *reinterpret_cast<const u32x2*>(prow + k0 + 8);
+      else
+        for (int e = 0; e < 4; ++e)
+          if (k0 + 8 + e < Nk) {
+            const uint16_t bits = reinterpret_cast<const uint16_t*>(prow)[k0 + 8 + e];
+            hi[e / 2] |= (uint32_t)bits << (16 * (e & 1));
+          }
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      const int rl = T::row_off(16 * j4), rh = T::row_off(16 * j4 + 8);
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+        const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4*)(vp + tbase + rl + 64 * mb));
+        const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4*)(vp + tbase + rh + 64 * mb));
+        const bf16x8 av = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        o[mb] = mfma_32x32x16_bf16(av, pb, o[mb]);
+      }
+    }
+  }
+  if (row < Nq) {
+    __bf16* orow = O + (bh * Nq + row) * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 pr;
+        pr[0] = pack_bf16x2(o[mb][4 * g], o[mb][4 * g + 1]);
+        pr[1] = pack_bf16x2(o[mb][4 * g + 2], o[mb][4 * g + 3]);
+        *reinterpret_cast<u32x2*>(orow + 32 * mb + 8 * g + 4 * h) = pr;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch(const NaiveArgs& a) {
+  const long qblocks = (long)((a.Nq + 127) / 128) * a.Hq * a.B;
+  _Float16* S = static_cast<_Float16*>(a.ws);
+  hipLaunchKernelGGL((naive_scores_kernel<D>), dim3((unsigned)qblocks),
+                     dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.q),
+                     static_cast<const __bf16*>(a.k), S, a.B, a.Hq, a.Hkv, a.Nq,
+                     a.Nk, a.scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned rows = (unsigned)((long)a.B * a.Hq * a.Nq);
+  const int nv = (a.Nk + kThreads - 1) / kThreads;
+  if (nv <= 8)
+    hipLaunchKernelGGL((naive_softmax_kernel<8>), dim3(rows), dim3(kThreads), 0,
+                       a.stream, S, a.lse, a.Nq, a.Nk, a.causal);
+  else if (nv <= 16)
+    hipLaunchKernelGGL((naive_softmax_kernel<16>), dim3(rows), dim3(kThreads), 0,
+                       a.stream, S, a.lse, a.Nq, a.Nk, a.causal);
+  else if (nv <= 32)
+    hipLaunchKernelGGL((naive_softmax_kernel<32>), dim3(rows), dim3(kThreads), 0,
+                       a.stream, S, a.lse, a.Nq, a.Nk, a.causal);
+  else
+    hipLaunchKernelGGL((naive_softmax_kernel<64>), dim3(rows), dim3(kThreads), 0,
+                       a.stream, S, a.lse, a.Nq, a.Nk, a.causal);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((naive_pv_kernel<D>), dim3((unsigned)qblocks), dim3(kThreads),
+                     0, a.stream, reinterpret_cast<const __bf16*>(S),
+                     static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o),
+                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t naive_workspace_bytes(int B, int Hq, int Nq, int Nk) {
+  return (size_t)B * Hq * Nq * Nk * 2;
+}
+
+hipError_t launch_naive_bf16(const NaiveArgs& a) {
+  return a.d == 128 ? launch<128>(a) : launch<64>(a);
+}
+
+}  // namespace fa

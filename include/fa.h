@@ -12,6 +12,8 @@
  *                    split over workgroups and merged by log-sum-exp.
  *   fa_paged_decode_fp8kv  the same over a cache stored as e4m3 codes with
  *                    per-tensor scales (half the bytes to read).
+ *   fa_naive_attention  the pages' three-kernel contrast: S and P
+ *                    materialised in device memory (for measurement).
  *
  * Sources (cited by page and section):
  *   [FA3-guide]  "Flash Attention 3 指南：GPU IO 优化的终极武器"
@@ -242,6 +244,33 @@ int fa_paged_decode_fp8kv(const void* q, const void* k_pool,
                           const float* kv_descale, void* o, float* lse,
                           void* workspace, size_t workspace_bytes,
                           int num_splits, void* stream);
+
+/*
+ * fa_naive_workspace_size - bytes of workspace fa_naive_attention needs:
+ * the B*Hq*Nq*Nk score matrix at 2 bytes per score. 0 for sizes <= 0.
+ */
+size_t fa_naive_workspace_size(int B, int Hq, int Nq, int Nk);
+
+/*
+ * fa_naive_attention - the same result as fa_fwd (bf16), computed the way
+ * the pages' contrast does it ([Capstone §0] and §1.1): three kernels with
+ * the score matrix S and the probabilities P written to and read back from
+ * device memory, 8*Nq*d + 8*Nq*Nk bytes per head (2-byte elements) instead
+ * of the fused kernel's single pass. Kept for measurement; use fa_fwd.
+ *   kernel 1: S = scale * Q K^T, stored as fp16 in `workspace`
+ *   kernel 2: per row, the three-pass safe softmax ([Capstone §2.1]) with
+ *             the causal mask; P (bf16) written over S's row, LSE written
+ *   kernel 3: O = P V
+ * Arguments as fa_fwd with dtype bf16, plus:
+ * Nk           a multiple of 8, at most 16384.
+ * workspace    device memory of fa_naive_workspace_size(B, Hq, Nq, Nk)
+ *              bytes, 256-byte aligned (contents on entry do not matter);
+ *              workspace_bytes its true size.
+ */
+int fa_naive_attention(const void* q, const void* k, const void* v, void* o,
+                       float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                       int d, float scale, int causal, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* fa_strerror - static, NUL-terminated description of a return code. */
 const char* fa_strerror(int code);

@@ -238,3 +238,32 @@ def dec8(**kw):
 ])
 def test_decode_fp8kv_rejects(lib, kw, code):
     assert dec8(**kw) == code
+
+
+def naive(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=8, Nk=64, d=128,
+             scale=0.1, causal=0, workspace=P, workspace_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return fa.fa_naive_attention(**a, check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), L.FA_EINVAL_NULL),
+    (dict(Nq=0), L.FA_EINVAL_DIM),
+    (dict(Nk=60), L.FA_EINVAL_DIM),          # not a multiple of 8
+    (dict(Nk=16392), L.FA_EINVAL_DIM),       # above 16384
+    (dict(d=80), L.FA_EUNSUPPORTED_D),
+    (dict(Hq=3, Hkv=2), L.FA_EGQA),
+    (dict(scale=-1.0), L.FA_ESCALE),
+    (dict(o=P + 4), L.FA_EALIGN),
+    (dict(workspace=None), L.FA_EWORKSPACE),
+    (dict(workspace_bytes=100), L.FA_EWORKSPACE),
+])
+def test_naive_rejects(lib, kw, code):
+    assert naive(**kw) == code
+
+
+def test_naive_workspace_size(lib):
+    assert fa.fa_naive_workspace_size(2, 3, 5, 64) == 2 * 3 * 5 * 64 * 2
+    assert fa.fa_naive_workspace_size(1, 1, 0, 8) == 0

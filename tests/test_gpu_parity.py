@@ -354,3 +354,42 @@ def test_decode_fp8_cache_full_workload(fa):
     o, lse = _gpu_decode_fp8(fa, di)
     ro, rl = _oracle_decode_fp8(di)
     _compare(o, lse, ro, rl, "bf16", name + " e4m3 cache")
+
+
+# ------------------------------------------------- naive three-kernel path
+# The contrast path materialises S (fp16) and P (bf16) in device memory.
+# Its own arithmetic sets its bar: P is normalised before it is rounded to
+# bf16, so the stored weights sum to 1 only within 2^-9 per weight, and O
+# can be off by up to 2^-9 * max|V| (~0.009 for these N(0,1) inputs) on
+# top of the bf16 rounding of O itself (<= 0.0078 below 4); S in fp16 moves
+# each score by <= 2^-11 |s|, so LSE by at most ~0.004 for |s| < 8.
+TOL["naive"] = (2e-2, 4e-3)
+def _gpu_naive(fa, inp):
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    o = torch.full((B, Hq, Nq, d), float("nan"), dtype=torch.bfloat16,
+                   device=dev)
+    lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32,
+                     device=dev)
+    ws = torch.empty(fa.fa_naive_workspace_size(B, Hq, Nq, Nk),
+                     dtype=torch.uint8, device=dev)
+    fa.fa_naive_attention(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, inp.scale,
+                          inp.causal, ws, ws.numel())
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal", [
+    (1, 2, 2, 256, 256, 128, False),
+    (1, 4, 2, 200, 200, 128, True),
+    (2, 2, 1, 130, 96, 64, True),       # Nq > Nk: early rows see no key
+    (1, 2, 2, 77, 304, 64, False),
+])
+def test_naive_matches_oracle(fa, B, Hq, Hkv, Nq, Nk, d, causal):
+    inp = W.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", causal=causal,
+                           seed=Nq + Nk)
+    o, lse = _gpu_naive(fa, inp)
+    ro, rl = _oracle_fwd(inp)
+    _compare(o, lse, ro, rl, "naive", f"naive {Nq}x{Nk} d{d} causal={causal}")
