@@ -1,20 +1,20 @@
 // fa_fwd_bf16.hip - exact attention forward, bf16 in / bf16 out, gfx950.
 //
-// One workgroup (4 waves) owns a 128-row query tile of one (batch, head)
-// and streams the key/value range in 64-key tiles: the Q-outer / KV-inner
-// order of [Capstone §4.1] with O, m, l held on chip and O divided by l
-// once at the end ([Capstone §4.2]). Q K^T and P V run on
+// One workgroup (8 waves, one per CU) owns a 256-row query tile of one
+// (batch, head) and streams the key/value range in 64-key tiles: the
+// Q-outer / KV-inner order of [Capstone §4.1] with O, m, l held on chip and
+// O divided by l once at the end ([Capstone §4.2]). Q K^T and P V run on
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation; S and P never leave
 // registers. Causal tiles above the diagonal are not visited
 // ([Capstone §7.3 Q2]); the tiles that cross it are masked per element.
 //
-// Data flow per key tile (double-buffered LDS, one barrier per tile):
-//   global K, V (16 B per lane) -> VGPRs (prefetched one tile ahead,
-//   overlapping the MFMA work of the current tile) -> LDS, both row-major
-//   with padded rows
-//   -> per wave: S^T = K Q^T (Q lives in VGPRs for the whole tile),
-//      online softmax, P^T packed to bf16 in registers, O^T += V^T P^T with
-//      the V^T operand produced by gfx950's LDS transpose read.
+// Data flow per key tile (one barrier per tile):
+//   global K, V -> LDS by direct loads (no VGPR staging), K two tiles ahead
+//   in two buffers, V two tiles ahead in three
+//   -> per wave (32 rows): S^T = K Q^T (Q lives in VGPRs), online softmax,
+//      P^T packed to bf16 in registers, O^T += V^T P^T with the V^T operand
+//      produced by gfx950's LDS transpose read. S(t+1) is computed while
+//      P(t) is formed.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -23,10 +23,11 @@
 namespace fa {
 namespace {
 
-constexpr int kBM = 128;       // query rows per workgroup (32 per wave)
+constexpr int kBM = 256;       // query rows per workgroup (32 per wave)
 constexpr int kBN = 64;        // keys per tile
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kThreads = 512;  // 8 waves: one workgroup per CU
 constexpr int kWaves = kThreads / 64;
+constexpr int kVStages = 3;    // V buffers: V is loaded kVStages-1 tiles ahead
 
 // ------------------------------------------------------------ LDS layout
 // K and V tiles (64 rows x d) arrive by direct global->LDS loads
@@ -80,13 +81,15 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) char k_lds1[T::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v_lds0[T::V_BYTES];
   __shared__ __attribute__((aligned(16))) char v_lds1[T::V_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds2[kVStages > 2 ? T::V_BYTES : 16];
   auto kbuf = [&](auto b) -> lds_char* {
     if constexpr (decltype(b)::value == 0) return (lds_char*)k_lds0;
     else return (lds_char*)k_lds1;
   };
   auto vbuf = [&](auto b) -> lds_char* {
     if constexpr (decltype(b)::value == 0) return (lds_char*)v_lds0;
-    else return (lds_char*)v_lds1;
+    else if constexpr (decltype(b)::value == 1) return (lds_char*)v_lds1;
+    else return (lds_char*)v_lds2;
   };
 
   const int tid = threadIdx.x;
@@ -199,13 +202,15 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
     return CAUSAL && (tile * kBN > wrow0 + 31 + off);
   };
 
-  // ---- prologue: K(0), V(0), K(1) in flight; S(0)
+  // ---- prologue: K(0), V(0), K(1) (and V(1) with three V buffers) in
+  // flight; S(0)
   constexpr std::integral_constant<int, 0> B0{};
   constexpr std::integral_constant<int, 1> B1{};
   if (nt > 0) {
     issue_k(0, B0);
     issue_v(0, B0);
     if (nt > 1) issue_k(1, B1);
+    if (kVStages > 2 && nt > 1) issue_v(1, B1);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -216,16 +221,21 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   // One key tile: S(t) arrives in sc; S(t+1) is computed into sn while P(t)
   // is formed. Tiles are taken in pairs with the two score buffers swapping
   // roles, so no tile ends with a register copy.
-  // `par` is t % 2 as a compile-time index.
-  auto step = [&](int t, auto par, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  // `par` is t % 2 and `vst` t % kVStages as compile-time indices.
+  auto step = [&](int t, auto par, auto vst, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     constexpr int P = decltype(par)::value;
+    constexpr int VS = decltype(vst)::value;
     constexpr std::integral_constant<int, P> cur{};
     constexpr std::integral_constant<int, 1 - P> nxt{};
+    constexpr std::integral_constant<int, VS> vcur{};
+    constexpr std::integral_constant<int, (VS + kVStages - 1) % kVStages> vnew{};
     const int n0 = t * kBN;
-    // K runs two tiles ahead, V one: both target buffers were last read
-    // before the previous barrier.
-    if (t + 2 < nt) issue_k(t + 2, cur);
-    if (t + 1 < nt) issue_v(t + 1, nxt);
+    // K runs two tiles ahead, V kVStages - 1: both target buffers were last
+    // read before the previous barrier.
+    const bool more_k = t + 2 < nt;
+    const bool more_v = t + kVStages - 1 < nt;
+    if (more_k) issue_k(t + 2, cur);
+    if (more_v) issue_v(t + kVStages - 1, vnew);
     const bool do_t = !skip_tile(t);
     if (do_t) {
       // mask the ragged end of the key range and the causal diagonal
@@ -255,11 +265,14 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
       // without a branch (so both sit in one basic block and interleave):
       // past the last tile, or beyond this wave's causal rows, the result is
       // never read, and the K buffer it reads is not being written.
+      // raised issue priority while this wave feeds the matrix cores: the
+      // other wave of the SIMD (another workgroup) fills in with its VALU work
+      __builtin_amdgcn_s_setprio(1);
       qk(nxt, sn);
       softmax_exp_pack<2>(sc, st, c, pw);
       // O^T += V^T P^T, 16 keys per MFMA: lane half h contracts keys
       // 32kb + 16j + 4h + {0..3} (items 0..3) and +8 (items 4..7)
-      const lds_char* vp0 = vbuf(cur) + vfrag;
+      const lds_char* vp0 = vbuf(vcur) + vfrag;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -280,14 +293,30 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
             o[mb] = mfma_32x32x16_bf16(a, pb, o[mb]);
           }
         }
+      __builtin_amdgcn_s_setprio(0);
     }
-    wait_vm0();
+    // tile t+1 needs K(t+2) and V(t+1); with three V buffers the V(t+2)
+    // loads just issued (the last BPW in flight) may still be pending
+    if (kVStages > 2 && more_v) __builtin_amdgcn_s_waitcnt(0x0F70 | T::BPW);
+    else wait_vm0();
     __syncthreads();
   };
   f32x16 sb[2];
-  for (int t = 0; t < nt; t += 2) {
-    step(t, B0, sc, sb);
-    if (t + 1 < nt) step(t + 1, B1, sb, sc);
+  constexpr std::integral_constant<int, 2> B2{};
+  if constexpr (kVStages == 2) {
+    for (int t = 0; t < nt; t += 2) {
+      step(t, B0, B0, sc, sb);
+      if (t + 1 < nt) step(t + 1, B1, B1, sb, sc);
+    }
+  } else {
+    for (int t = 0; t < nt; t += 6) {
+      step(t, B0, B0, sc, sb);
+      if (t + 1 < nt) step(t + 1, B1, B1, sb, sc);
+      if (t + 2 < nt) step(t + 2, B0, B2, sc, sb);
+      if (t + 3 < nt) step(t + 3, B1, B0, sb, sc);
+      if (t + 4 < nt) step(t + 4, B0, B1, sc, sb);
+      if (t + 5 < nt) step(t + 5, B1, B2, sb, sc);
+    }
   }
 
   // ---- epilogue: O = O^T / lr, LSE = ln 2 * (m + log2 l)
