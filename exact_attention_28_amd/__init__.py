@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     fa_paged_decode,
     fa_paged_decode_fp8kv,
     fa_paged_decode_workspace_size,
+    fa_paged_prefill,
     fa_strerror,
     load_library,
 )

@@ -34,7 +34,7 @@ FA_EALIGN = -11
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_naive_attention",
            "fa_naive_workspace_size", "fa_paged_decode",
            "fa_paged_decode_fp8kv", "fa_paged_decode_workspace_size",
-           "fa_strerror")
+           "fa_paged_prefill", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH):
     lib.fa_paged_decode.restype = i
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                     f, vp, vp, vp, sz, i, vp]
+    lib.fa_paged_prefill.restype = i
+    lib.fa_paged_prefill.argtypes = [vp] * 5 + [i] * 8 + [f, i, vp, vp, vp]
     lib.fa_naive_attention.restype = i
     lib.fa_naive_attention.argtypes = [vp] * 5 + [i] * 6 + [f, i, vp, sz, vp]
     lib.fa_naive_workspace_size.restype = sz
@@ -209,6 +211,20 @@ def fa_naive_attention(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq),
         int(Hkv), int(Nq), int(Nk), int(d), float(scale), int(bool(causal)),
         _ptr(workspace), int(workspace_bytes), _stream(stream, q, o))
+    if check:
+        _check(code)
+    return code
+
+
+def fa_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, page_size,
+                     num_pages, B, Hq, Hkv, Nq, d, max_pages_per_seq, scale,
+                     causal, o, lse, stream=None, check=True) -> int:
+    """Chunked prefill against a paged cache (see include/fa.h)."""
+    code = load_library().fa_paged_prefill(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        _ptr(seq_lens), int(page_size), int(num_pages), int(B), int(Hq),
+        int(Hkv), int(Nq), int(d), int(max_pages_per_seq), float(scale),
+        int(bool(causal)), _ptr(o), _ptr(lse), _stream(stream, q, o))
     if check:
         _check(code)
     return code

@@ -14,6 +14,7 @@ namespace {
 
 constexpr long kMaxIndex = 0x7fffffffL;  // 32-bit element offsets per head
 constexpr int kMaxRanges = 65536;        // decode page ranges per KV head
+constexpr int kMaxPrefillPages = 8192;   // pages per request, paged prefill
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -216,6 +217,50 @@ int fa_naive_attention(const void* q, const void* k, const void* v, void* o,
   a.ws = workspace;
   a.stream = static_cast<hipStream_t>(stream);
   return (int)fa::launch_naive_bf16(a);
+}
+
+int fa_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     int page_size, int num_pages, int B, int Hq, int Hkv,
+                     int Nq, int d, int max_pages_per_seq, float scale,
+                     int causal, void* o, float* lse, void* stream) {
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o)
+    return FA_EINVAL_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || max_pages_per_seq <= 0)
+    return FA_EINVAL_DIM;
+  if (d != 64 && d != 128) return FA_EUNSUPPORTED_D;
+  if (Hq % Hkv != 0) return FA_EGQA;
+  if (page_size != 16 || num_pages <= 0) return FA_EPAGE;
+  if (max_pages_per_seq > kMaxPrefillPages) return FA_EINVAL_DIM;
+  if (!(isfinite(scale) && scale > 0.f)) return FA_ESCALE;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(o) || ((uintptr_t)lse & 3u) != 0 ||
+      ((uintptr_t)block_table & 3u) != 0 || ((uintptr_t)seq_lens & 3u) != 0)
+    return FA_EALIGN;
+  if ((long)Nq * d > kMaxIndex || numel4(B, Hq, Nq, d) < 0) return FA_EINVAL_DIM;
+  if (numel4(num_pages, page_size, Hkv, d) < 0) return FA_EINVAL_DIM;
+  if ((long)B * max_pages_per_seq > kMaxIndex) return FA_EINVAL_DIM;
+  long blocks;
+  if (!mul_ok((Nq + 127) / 128, (long)Hq * B, &blocks) || blocks > kMaxIndex)
+    return FA_EINVAL_DIM;
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k_pool;
+  a.v = v_pool;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = 0;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.s_q = a.s_k = a.s_v = 1.f;
+  a.stream = static_cast<hipStream_t>(stream);
+  return (int)fa::launch_paged_prefill_bf16(a, block_table, seq_lens,
+                                            max_pages_per_seq, num_pages);
 }
 
 static int decode_check(int B, int Hq, int Hkv, int d, int max_pages,

@@ -66,12 +66,24 @@ __device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
 // s_waitcnt vmcnt(0): the direct loads of this wave have reached LDS.
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int D, bool CAUSAL>
+// Where K and V come from. Contiguous: [B, Hkv, Nk, d]. Paged (the
+// chunked prefill of [FA3-paged §3.2]): the cache of request b is
+// seq_lens[b] tokens in 16-token pages of a [num_pages, 16, Hkv, d] pool,
+// logical page p at physical page block_table[b, p]; the Nq queries are the
+// request's last Nq positions (bottom-right causal alignment).
+struct PagedKV {
+  const int32_t* bt;  // [B, max_pages]
+  const int32_t* sl;  // [B]
+  int max_pages, num_pages;
+};
+constexpr int kMaxPagesLds = 8192;  // page-table entries a workgroup stages
+
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,
-    float c) {
+    float c, PagedKV pk) {
   using T = Lay<D>;
   // Four separate arrays, always selected by a compile-time index: the
   // compiler can then tell that reading one buffer does not depend on the
@@ -103,11 +115,36 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   const int hk = ti.hq / (Hq / Hkv);
   const int q0 = ti.qt * kBM;
   const long qbase = (long)(ti.b * Hq + ti.hq) * Nq * D;
-  const __bf16* Kh = K + (long)(ti.b * Hkv + hk) * Nk * D;
-  const __bf16* Vh = V + (long)(ti.b * Hkv + hk) * Nk * D;
-  const int off = Nk - Nq;  // bottom-right causal alignment
-  int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(q0 + kBM, Nq) + off);
+  // keys of this request; for the paged cache its length, and the page
+  // table staged in LDS (ids outside the pool are replaced by 0 and turn
+  // the request's output to NaN)
+  __shared__ int page_ids[PAGED ? kMaxPagesLds : 1];
+  __shared__ int page_bad;
+  int nk = Nk;
+  if constexpr (PAGED) {
+    nk = max(0, min(pk.sl[ti.b], pk.max_pages * 16));
+    const int np = (nk + 15) / 16;
+    if (tid == 0) page_bad = 0;
+    __syncthreads();
+    bool bad = false;
+    for (int i = tid; i < np; i += kThreads) {
+      const int id = pk.bt[(long)ti.b * pk.max_pages + i];
+      const bool ok = id >= 0 && id < pk.num_pages;
+      page_ids[i] = ok ? id : 0;
+      bad |= !ok;
+    }
+    if (bad) page_bad = 1;
+    __syncthreads();
+  }
+  // contiguous: the head's K/V; paged: the pool plus this head's offset
+  // within a token row (rows of a page are Hkv * d apart)
+  const long kv_head = PAGED ? (long)hk * D : (long)(ti.b * Hkv + hk) * Nk * D;
+  const __bf16* Kh = K + kv_head;
+  const __bf16* Vh = V + kv_head;
+  const long tok_stride = PAGED ? (long)Hkv * D : D;
+  const int off = nk - Nq;  // bottom-right causal alignment
+  int kend = nk;
+  if (CAUSAL) kend = min(nk, min(q0 + kBM, Nq) + off);
   const int nt = kend > 0 ? (kend + kBN - 1) / kBN : 0;
 
   // Q fragments (B operand of S^T = K Q^T): row r32 of this wave's 32
@@ -143,35 +180,42 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
     koff[i] = k_row(w + kWaves * i) * D + 8 * chunk;
     voff[i] = v_row(w + kWaves * i) * D + 8 * chunk;
   }
+  // element offset of tile-relative row r of tile n0 (rows past the keys
+  // clamped to the last key: their scores are masked, their P is 0)
+  auto row_elem = [&](int n0, int r) -> long {
+    const int t = n0 + min(r, nk - 1 - n0);
+    if constexpr (PAGED)
+      return ((long)page_ids[t >> 4] * 16 + (t & 15)) * tok_stride;
+    else
+      return (long)t * D;
+  };
   auto issue_k = [&](int tile, auto buf) {
     const int n0 = tile * kBN;
-    const __bf16* src = Kh + (long)n0 * D;
     lds_char* dst = kbuf(buf) + w * T::KPITCH;
-    if (n0 + kBN <= Nk) {
+    if (!PAGED && n0 + kBN <= nk) {
+      const __bf16* src = Kh + (long)n0 * D;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
         g2lds_16B(src + koff[i], dst + kWaves * i * T::KPITCH);
     } else {
-      const int last = Nk - 1 - n0;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(src + min(k_row(w + kWaves * i), last) * D + 8 * chunk,
+        g2lds_16B(Kh + row_elem(n0, k_row(w + kWaves * i)) + 8 * chunk,
                   dst + kWaves * i * T::KPITCH);
     }
   };
   auto issue_v = [&](int tile, auto buf) {
     const int n0 = tile * kBN;
-    const __bf16* src = Vh + (long)n0 * D;
     lds_char* dst = vbuf(buf) + w * T::VPITCH;
-    if (n0 + kBN <= Nk) {
+    if (!PAGED && n0 + kBN <= nk) {
+      const __bf16* src = Vh + (long)n0 * D;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
         g2lds_16B(src + voff[i], dst + kWaves * i * T::VPITCH);
     } else {
-      const int last = Nk - 1 - n0;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(src + min(v_row(w + kWaves * i), last) * D + 8 * chunk,
+        g2lds_16B(Vh + row_elem(n0, v_row(w + kWaves * i)) + 8 * chunk,
                   dst + kWaves * i * T::VPITCH);
     }
   };
@@ -240,9 +284,9 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
     if (do_t) {
       // mask the ragged end of the key range and the causal diagonal
       const bool need_mask =
-          (n0 + kBN > Nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
+          (n0 + kBN > nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
       if (need_mask) {
-        const int lim = CAUSAL ? min(Nk - 1, row + off) : Nk - 1;
+        const int lim = CAUSAL ? min(nk - 1, row + off) : nk - 1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -324,7 +368,10 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   const float lrtot = sum_halves(st.lr);
   if (row < Nq) {
     const bool live = ltot > 0.f;
-    const float inv = live ? 1.f / lrtot : 0.f;
+    float inv = live ? 1.f / lrtot : 0.f;
+    bool nan_out = false;
+    if constexpr (PAGED) nan_out = page_bad != 0;
+    if (nan_out) inv = __builtin_nanf("");
     __bf16* orow = O + qbase + (long)row * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
@@ -337,29 +384,41 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
       }
     if (h == 0 && LSE != nullptr)
       LSE[(long)(ti.b * Hq + ti.hq) * Nq + row] =
-          live ? (st.m + fast_log2(ltot)) * kLn2 : kNegInf;
+          nan_out ? __builtin_nanf("")
+                  : (live ? (st.m + fast_log2(ltot)) * kLn2 : kNegInf);
   }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const FwdArgs& a) {
+template <int D, bool CAUSAL, bool PAGED>
+hipError_t launch(const FwdArgs& a, const PagedKV& pk) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
   const long blocks = (long)n_qt * a.Hq * a.B;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PAGED>), dim3((unsigned)blocks),
                      dim3(kThreads), 0, a.stream,
                      static_cast<const __bf16*>(a.q),
                      static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v),
                      static_cast<__bf16*>(a.o), a.lse, a.B, a.Hq, a.Hkv, a.Nq,
-                     a.Nk, a.scale * kLog2e);
+                     a.Nk, a.scale * kLog2e, pk);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch<128, true>(a) : launch<128, false>(a);
-  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+  const PagedKV none{nullptr, nullptr, 0, 0};
+  if (a.d == 128)
+    return a.causal ? launch<128, true, false>(a, none) : launch<128, false, false>(a, none);
+  return a.causal ? launch<64, true, false>(a, none) : launch<64, false, false>(a, none);
+}
+
+hipError_t launch_paged_prefill_bf16(const FwdArgs& a, const int32_t* bt,
+                                     const int32_t* sl, int max_pages,
+                                     int num_pages) {
+  const PagedKV pk{bt, sl, max_pages, num_pages};
+  if (a.d == 128)
+    return a.causal ? launch<128, true, true>(a, pk) : launch<128, false, true>(a, pk);
+  return a.causal ? launch<64, true, true>(a, pk) : launch<64, false, true>(a, pk);
 }
 
 }  // namespace fa

@@ -57,6 +57,11 @@ hipError_t launch_naive_bf16(const NaiveArgs& a);
 
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+// The bf16 forward over a paged cache: a.k, a.v are the pools, a.Nk unused;
+// keys of request b are seq_lens[b] tokens through block_table.
+hipError_t launch_paged_prefill_bf16(const FwdArgs& a, const int32_t* bt,
+                                     const int32_t* sl, int max_pages,
+                                     int num_pages);
 hipError_t launch_fwd_fp8(const FwdArgs& a);
 
 struct DecodeArgs {

@@ -12,6 +12,8 @@
  *                    split over workgroups and merged by log-sum-exp.
  *   fa_paged_decode_fp8kv  the same over a cache stored as e4m3 codes with
  *                    per-tensor scales (half the bytes to read).
+ *   fa_paged_prefill chunked prefill: a block of new query tokens per
+ *                    request against its paged KV cache.
  *   fa_naive_attention  the pages' three-kernel contrast: S and P
  *                    materialised in device memory (for measurement).
  *
@@ -244,6 +246,37 @@ int fa_paged_decode_fp8kv(const void* q, const void* k_pool,
                           const float* kv_descale, void* o, float* lse,
                           void* workspace, size_t workspace_bytes,
                           int num_splits, void* stream);
+
+/*
+ * fa_paged_prefill - exact attention of Nq new query tokens per request
+ * against the request's paged KV cache (chunked prefill: the serving use
+ * of the paged cache of [FA3-paged §3.2]), in the fused single pass of
+ * fa_fwd (S and P stay on chip).
+ *
+ * Request b's cache holds L = seq_lens[b] tokens (clamped to
+ * [0, max_pages_per_seq * 16]) in the pages block_table[b, 0..ceil(L/16)),
+ * and q holds its last Nq positions, L-Nq .. L-1 (they are already in the
+ * cache). causal non-zero: query i sees keys j <= i + L - Nq (bottom-right
+ * alignment; rows with i + L - Nq < 0 see no key: O = 0, LSE = -inf);
+ * zero: every query sees all L keys.
+ *
+ * q            [B, Hq, Nq, d] bf16
+ * k_pool,
+ * v_pool       [num_pages, page_size, Hkv, d] bf16 (as fa_paged_decode)
+ * block_table  [B, max_pages_per_seq] int32; entries past ceil(L/16) are
+ *              not read; max_pages_per_seq <= 8192. A referenced page id
+ *              outside [0, num_pages) is not dereferenced: that request's
+ *              O and LSE become NaN.
+ * seq_lens     [B] int32
+ * page_size    16.  Hq % Hkv == 0; scale finite and > 0.
+ * o            [B, Hq, Nq, d] bf16; lse [B, Hq, Nq] fp32 or NULL.
+ * No workspace. stream hipStream_t or NULL.
+ */
+int fa_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     int page_size, int num_pages, int B, int Hq, int Hkv,
+                     int Nq, int d, int max_pages_per_seq, float scale,
+                     int causal, void* o, float* lse, void* stream);
 
 /*
  * fa_naive_workspace_size - bytes of workspace fa_naive_attention needs:

@@ -12,6 +12,7 @@ from .attention import (  # noqa: F401
     online_softmax_stats,
     paged_decode,
     paged_decode_fp8,
+    paged_prefill,
     safe_softmax,
     softmax_stats,
 )

@@ -68,6 +68,7 @@ __all__ = [
     "gather_paged_kv",
     "paged_decode",
     "paged_decode_fp8",
+    "paged_prefill",
     "attention_backward",
 ]
 
@@ -277,6 +278,26 @@ def paged_decode_fp8(q, k_codes, v_codes, s_k, s_v, block_table, seq_lens,
     kx = np.asarray(k_codes, dtype=np.float64) * float(s_k)
     vx = np.asarray(v_codes, dtype=np.float64) * float(s_v)
     return paged_decode(q, kx, vx, block_table, seq_lens, page_size, scale)
+
+
+def paged_prefill(q, k_pool, v_pool, block_table, seq_lens, page_size, scale,
+                  causal=True):
+    """Chunked prefill against a paged cache ([FA3-paged §3.2] pages): the
+    Nq queries of request r are its last Nq positions, so with the cache
+    gathered back to [Hkv, L, d] this is ``attention`` with Nk = L, whose
+    bottom-right causal alignment lets query i see keys j <= i + L - Nq.
+    q: [B, Hq, Nq, d]. Returns (O [B, Hq, Nq, d], LSE [B, Hq, Nq])."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, Nq, d = q.shape
+    out = np.zeros((B, Hq, Nq, d), dtype=np.float64)
+    lse = np.full((B, Hq, Nq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        K = gather_paged_kv(k_pool, block_table[b], seq_lens[b], page_size)
+        V = gather_paged_kv(v_pool, block_table[b], seq_lens[b], page_size)
+        o, s = attention(q[b][None], K[None], V[None], scale, causal=causal)
+        out[b] = o[0]
+        lse[b] = s[0]
+    return out, lse
 
 
 # --------------------------------------------------------------------------

@@ -267,3 +267,29 @@ def test_naive_rejects(lib, kw, code):
 def test_naive_workspace_size(lib):
     assert fa.fa_naive_workspace_size(2, 3, 5, 64) == 2 * 3 * 5 * 64 * 2
     assert fa.fa_naive_workspace_size(1, 1, 0, 8) == 0
+
+
+def ppf(**kw):
+    a = dict(q=P, k_pool=P, v_pool=P, block_table=P, seq_lens=P, page_size=16,
+             num_pages=100, B=2, Hq=8, Hkv=2, Nq=64, d=128,
+             max_pages_per_seq=64, scale=0.1, causal=1, o=P, lse=P,
+             stream=None)
+    a.update(kw)
+    return fa.fa_paged_prefill(**a, check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), L.FA_EINVAL_NULL),
+    (dict(seq_lens=None), L.FA_EINVAL_NULL),
+    (dict(Nq=0), L.FA_EINVAL_DIM),
+    (dict(max_pages_per_seq=8193), L.FA_EINVAL_DIM),   # page table cap
+    (dict(d=32), L.FA_EUNSUPPORTED_D),
+    (dict(Hq=6, Hkv=4), L.FA_EGQA),
+    (dict(page_size=32), L.FA_EPAGE),
+    (dict(num_pages=0), L.FA_EPAGE),
+    (dict(scale=0.0), L.FA_ESCALE),
+    (dict(o=P + 2), L.FA_EALIGN),
+    (dict(block_table=P + 1), L.FA_EALIGN),
+])
+def test_paged_prefill_rejects(lib, kw, code):
+    assert ppf(**kw) == code

@@ -393,3 +393,69 @@ def test_naive_matches_oracle(fa, B, Hq, Hkv, Nq, Nk, d, causal):
     o, lse = _gpu_naive(fa, inp)
     ro, rl = _oracle_fwd(inp)
     _compare(o, lse, ro, rl, "naive", f"naive {Nq}x{Nk} d{d} causal={causal}")
+
+
+# ------------------------------------------------ chunked (paged) prefill
+def _gpu_paged_prefill(fa, di, causal, num_pages=None):
+    dev = torch.device("cuda:0")
+    q = di.q.to(dev)
+    kp, vp = di.k_pool.to(dev), di.v_pool.to(dev)
+    bt, sl = di.block_table.to(dev), di.seq_lens.to(dev)
+    B, Hq, Nq, d = q.shape
+    npg, page, Hkv, _ = kp.shape
+    o = torch.full((B, Hq, Nq, d), float("nan"), dtype=torch.bfloat16,
+                   device=dev)
+    lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32,
+                     device=dev)
+    fa.fa_paged_prefill(q, kp, vp, bt, sl, page,
+                        npg if num_pages is None else num_pages, B, Hq, Hkv,
+                        Nq, d, bt.shape[1], di.scale, causal, o, lse)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (6, 2)])
+@pytest.mark.parametrize("nq", [1, 17, 256, 300])
+@pytest.mark.parametrize("causal", [True, False])
+def test_paged_prefill_matches_oracle(fa, d, hq, hkv, nq, causal):
+    lens = [0, 5, 16, 300, 1000, 777]
+    di = W.paged_prefill_inputs(len(lens), hq, hkv, d, nq, lens=lens,
+                                max_pages=70, seed=nq + d + hq,
+                                extra_pages=3)
+    o, lse = _gpu_paged_prefill(fa, di, causal)
+    ro, rl = oracle.paged_prefill(W.as_f64(di.q), W.as_f64(di.k_pool),
+                                  W.as_f64(di.v_pool), di.block_table.numpy(),
+                                  di.seq_lens.numpy(), di.page_size, di.scale,
+                                  causal=causal)
+    _compare(o, lse, ro, rl, "bf16",
+             f"paged prefill d{d} {hq}/{hkv} Nq={nq} causal={causal}")
+
+
+def test_paged_prefill_bad_page_gives_nan(fa):
+    di = W.paged_prefill_inputs(3, 8, 2, 128, 32, lens=[100, 100, 100],
+                                max_pages=8, seed=4)
+    bt = di.block_table.clone()
+    bt[1, 3] = 1_000_000
+    di.block_table = bt
+    o, lse = _gpu_paged_prefill(fa, di, True)
+    assert np.all(np.isnan(o[1])) and np.all(np.isnan(lse[1]))
+    assert not np.any(np.isnan(o[[0, 2]]))
+
+
+def test_paged_prefill_long_context_sampled(fa):
+    # 4 requests of 3000-8000 cached tokens, 512 new queries each (GQA 32/8):
+    # the last 16 rows of each chunk against the oracle
+    lens = [8000, 3000, 6513, 4096]
+    di = W.paged_prefill_inputs(4, 32, 8, 128, 512, lens=lens,
+                                max_pages=512, seed=31)
+    o, lse = _gpu_paged_prefill(fa, di, True)
+    q = W.as_f64(di.q)[:, :, -16:]
+    ro, rl = oracle.paged_prefill(q, W.as_f64(di.k_pool), W.as_f64(di.v_pool),
+                                  di.block_table.numpy(),
+                                  di.seq_lens.numpy(), 16, di.scale,
+                                  causal=True)
+    # the oracle's 16-row chunk is the last 16 positions too, so the causal
+    # alignment is the same
+    _compare(o[:, :, -16:], lse[:, :, -16:], ro, rl, "bf16",
+             "paged prefill long, last 16 rows")

@@ -486,6 +486,32 @@ def test_paged_decode_fp8_cache_scales():
     assert np.max(np.abs(l2 - lse)) < 1e-12
 
 
+def test_paged_prefill_rows_are_decodes_of_prefixes():
+    # causal chunked prefill: query i of the chunk is the token at position
+    # L - Nq + i, so it is the decode of the request's first L - Nq + i + 1
+    # cached tokens (an independent route: paged_decode with shorter lengths)
+    import workloads as W
+    di = W.paged_prefill_inputs(3, 4, 2, 8, 5, lens=[40, 5, 17], max_pages=4,
+                                seed=12)
+    q = W.as_f64(di.q)
+    kp, vp = W.as_f64(di.k_pool), W.as_f64(di.v_pool)
+    bt, sl = di.block_table.numpy(), di.seq_lens.numpy()
+    o, lse = oracle.paged_prefill(q, kp, vp, bt, sl, 16, 0.3, causal=True)
+    for i in range(5):
+        lens_i = np.maximum(sl - 5 + i + 1, 0)
+        od, ld = oracle.paged_decode(q[:, :, i], kp, vp, bt, lens_i, 16, 0.3)
+        assert np.max(np.abs(od - o[:, :, i])) < 1e-12
+        live = np.isfinite(ld)
+        assert np.array_equal(live, np.isfinite(lse[:, :, i]))
+        assert np.max(np.abs(ld[live] - lse[:, :, i][live])) < 1e-12
+    # non-causal: every query of a request sees all of its L tokens, the
+    # same as a decode of each query against the full cache
+    o2, _ = oracle.paged_prefill(q, kp, vp, bt, sl, 16, 0.3, causal=False)
+    for i in range(5):
+        od, _ = oracle.paged_decode(q[:, :, i], kp, vp, bt, sl, 16, 0.3)
+        assert np.max(np.abs(od - o2[:, :, i])) < 1e-12
+
+
 # ---------------------------------------------------------------- backward
 # The gradient of the definition is pinned by numerical differentiation of
 # the forward oracle (central differences in fp64 on tiny inputs, an

@@ -206,3 +206,16 @@ def upstream_grad(shape, seed=4242, dtype="bf16") -> torch.Tensor:
     g = rng.standard_normal(tuple(shape), dtype=np.float32)
     t, _ = _to_storage(g, dtype)
     return t
+
+
+def paged_prefill_inputs(n_req, Hq, Hkv, d, Nq, lens, max_pages=None,
+                         seed=42, extra_pages=0):
+    """A paged cache (the decode recipe: K/V pools N(0,1) in bf16, seeded
+    page permutation, poisoned tail slots) plus Nq new query tokens per
+    request, q [n_req, Hq, Nq, d] ~ N(0,1) bf16 drawn from seed + 1."""
+    di = decode_inputs(n_req, Hq, Hkv, d, lens=lens, max_pages=max_pages,
+                       seed=seed, extra_pages=extra_pages)
+    rng = np.random.default_rng(seed + 1)
+    q = rng.standard_normal((n_req, Hq, Nq, d), dtype=np.float32)
+    di.q = torch.from_numpy(q).to(torch.bfloat16)
+    return di
