@@ -11,10 +11,12 @@ One step = one pass of the whole path over its synthetic workloads:
   5. workload 2 over a cache stored as e4m3 codes (fa_paged_decode_fp8kv)
   6. the non-causal bf16 prefill B=4, H=16, N=2048, d=128, fused (fa_fwd)
      and as the pages' three-kernel contrast (fa_naive_attention)
+  7. chunked prefill against the paged cache (fa_paged_prefill): 16
+     requests, 512 new tokens each, caches of U{4096..8192} tokens
 Inputs are seeded N(0,1) draws (seed 42) already resident in HBM when the
 timed region starts. Each launch is bracketed by HIP events on the stream
 it runs on; the step time is the wall time of K steps of legs 1-3 between
-two device synchronisations. Legs 4-6 are timed afterwards, K launches
+two device synchronisations. Legs 4-7 are timed afterwards, K launches
 each.
 
 Prints ONE JSON line. `value` is the bf16 causal prefill throughput in
@@ -150,7 +152,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs",
-                    default="prefill,decode,fp8,bwd,decode8,noncausal,naive",
+                    default="prefill,decode,fp8,bwd,decode8,noncausal,naive,"
+                    "chunked",
                     help="comma list of legs to run (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -277,6 +280,26 @@ def main():
             calls["naive"] = lambda: fa.fa_naive_attention(
                 qn, kn, vn, on, ln, *args_n, wsn, wsn.numel(), stream)
             info["naive"] = dict(flops=prefill_flops(cn), cfg=cn)
+    if "chunked" in legs:
+        # chunked prefill: a 512-token chunk for each of 16 requests against
+        # paged caches of U{4096..8192} tokens (the chunk's own positions
+        # included), Hq=32, Hkv=8, d=128, causal
+        import numpy as np
+        lens_c = np.random.default_rng(42).integers(4096, 8192, size=16,
+                                                    endpoint=True)
+        dc = W.paged_prefill_inputs(16, 32, 8, 128, 512, lens=list(lens_c),
+                                    max_pages=512, seed=42)
+        qc = dc.q.to(dev)
+        kpc, vpc = dc.k_pool.to(dev), dc.v_pool.to(dev)
+        btc, slc = dc.block_table.to(dev), dc.seq_lens.to(dev)
+        oc = torch.empty(qc.shape, dtype=torch.bfloat16, device=dev)
+        lc = torch.empty(qc.shape[:3], dtype=torch.float32, device=dev)
+        calls["chunked"] = lambda: fa.fa_paged_prefill(
+            qc, kpc, vpc, btc, slc, 16, kpc.shape[0], 16, 32, 8, 512, 128,
+            btc.shape[1], dc.scale, True, oc, lc, stream)
+        pairs = sum(sum(min(int(L), i + int(L) - 512 + 1) for i in range(512))
+                    for L in lens_c)
+        info["chunked"] = dict(flops=4.0 * 128 * pairs * 32)
     torch.cuda.synchronize()
     print(f"bench: inputs resident, legs={legs}", file=sys.stderr, flush=True)
 
@@ -284,7 +307,8 @@ def main():
     # leg is timed after it in a phase of its own, so its heat and power
     # draw do not change the clocks the forward legs run at
     order = [x for x in ("prefill", "decode", "fp8", "copy") if x in calls]
-    extra = [x for x in ("bwd", "decode8", "noncausal", "naive") if x in calls]
+    extra = [x for x in ("bwd", "decode8", "noncausal", "naive", "chunked")
+             if x in calls]
 
     def timed(names, steps):
         ev = {n: [] for n in names}
@@ -421,6 +445,17 @@ def main():
             "bf16_noncausal_fused"] = entry
         workload.append(f"bf16 prefill B={c['B']} H={c['Hq']} N={N} d={d} "
                         f"({'three-kernel contrast' if leg == 'naive' else 'fused'})")
+    if "chunked" in order:
+        t = statistics.mean(ms["chunked"]) / 1e3
+        tf = info["chunked"]["flops"] / t / 1e12
+        out["chunked_prefill"] = {
+            "value": tf, "unit": "TFLOPS", "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+            "kernel": "fwd_bf16_kernel<paged>", "launch_ms_mean": t * 1e3,
+            "launch_ms_min": min(ms["chunked"])}
+        workload.append("chunked prefill 16 requests x 512 new tokens, paged "
+                        "cache U{4096..8192}, Hq=32 Hkv=8 d=128")
+        if "value" not in out:
+            out["value"], out["unit"] = tf, "TFLOPS"
     if "copy" in order:
         t = statistics.mean(ms["copy"]) / 1e3
         out["copy_calibration"] = {"bytes_per_launch": info["copy"]["bytes"],
