@@ -51,11 +51,18 @@ __device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // A row-major tile of ROWS rows x D bf16 in LDS, as 1 KB blocks (one direct
-// load instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B; row r sits
-// in block r % NB at slot r / NB. Eight consecutive rows (the lanes one row
-// read serves together) fall in different blocks, so 16-byte row reads are
-// conflict free; the transpose reads (4 consecutive rows x 32 B per 16-lane
-// group) meet at most two-way conflicts.
+// load instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B. Two layouts
+// with one interface: row_off(r) + chunk_off(k) is the byte offset of the
+// 16-byte chunk k of row r, row_off(r) + col_off(x) that of byte x of row r,
+// and the direct load of block b moves chunk lane_chunk(lane) of row
+// block_row(b, lane) to byte 16 * lane of the block.
+//
+// RowTile: row r in block r % NB at slot r / NB. Sixteen consecutive rows
+// read at one chunk (the A operand of a row-major product) fall in sixteen
+// different blocks when NB >= 16, whose pitch spreads them over the banks;
+// reads of the transpose (4 consecutive rows x 64 B per 32-lane half) meet
+// up to 4-way conflicts. Used where a tile is only read by rows, and at
+// d = 64.
 template <int D, int ROWS>
 struct RowTile {
   static constexpr int RPB = 1024 / (2 * D);  // rows per block
@@ -64,22 +71,67 @@ struct RowTile {
   static constexpr int PITCH = 1040;
   static constexpr int BYTES = NB * PITCH;
   static constexpr int BPW = NB / kWaves;     // blocks each wave loads
-  static __device__ __forceinline__ int row_off(int r) {
+  static __device__ __forceinline__ constexpr int row_off(int r) {
     return (r % NB) * PITCH + (r / NB) * (2 * D);
+  }
+  static __device__ __forceinline__ constexpr int chunk_off(int k) { return 16 * k; }
+  static __device__ __forceinline__ constexpr int col_off(int x) { return x; }
+  static __device__ __forceinline__ int block_row(int b, int lane) {
+    return b + NB * (lane / CPR);
+  }
+  static __device__ __forceinline__ int lane_chunk(int lane) { return lane % CPR; }
+};
+
+// IlvTile (d = 128, tiles read both by rows and transposed): block b holds
+// rows 4b .. 4b + 3 with their chunks interleaved in 64-byte groups: chunk
+// k = 4a + c of row 4b + j sits at byte 256a + 64j + 16c of the block.
+//  * row reads: sixteen consecutive rows at one chunk are four blocks x four
+//    rows; block b adds 16 b (mod 256) and row j adds 64 j, so the sixteen
+//    16-byte pieces cover the 256 bytes of the banks once;
+//  * transpose reads: a 32-lane half reads 64 contiguous bytes of each of
+//    four consecutive rows 4b .. 4b + 3, which sit 64 B apart: again each
+//    bank once.
+// Both offsets stay one per-lane base plus compile-time constants (row_off
+// is additive over multiples of 4 rows, chunk_off over the chunk's bit 0
+// and col_off over multiples of 64 bytes).
+template <int ROWS>
+struct IlvTile {
+  static constexpr int NB = ROWS / 4;
+  static constexpr int PITCH = 1040;
+  static constexpr int BYTES = NB * PITCH;
+  static constexpr int BPW = NB / kWaves;
+  static __device__ __forceinline__ constexpr int row_off(int r) {
+    return (r / 4) * PITCH + 64 * (r % 4);
+  }
+  static __device__ __forceinline__ constexpr int chunk_off(int k) {
+    return 256 * (k / 4) + 16 * (k % 4);
+  }
+  static __device__ __forceinline__ constexpr int col_off(int x) {
+    return 256 * (x / 64) + x % 64;
+  }
+  static __device__ __forceinline__ int block_row(int b, int lane) {
+    return 4 * b + ((lane >> 2) & 3);
+  }
+  static __device__ __forceinline__ int lane_chunk(int lane) {
+    return 4 * (lane >> 4) + (lane & 3);
   }
 };
 
-// Issues the direct loads of one tile: rows [r0, r0 + ROWS) of a row-major
-// [n, D] matrix, rows at or past n clamped to the last one (never used).
+// The layout of a tile that is read both ways.
 template <int D, int ROWS>
+using TrTile = std::conditional_t<D == 128, IlvTile<ROWS>, RowTile<D, ROWS>>;
+
+// Issues the direct loads of one tile of layout T: rows [r0, r0 + rows) of
+// a row-major [n, D] matrix, rows at or past n clamped to the last one
+// (never used).
+template <int D, class T>
 __device__ __forceinline__ void load_tile(const __bf16* src, int r0, int n,
                                           lds_char* dst, int w, int lane) {
-  using T = RowTile<D, ROWS>;
-  const int slot = lane / T::CPR, chunk = lane % T::CPR;
+  const int chunk = T::lane_chunk(lane);
 #pragma unroll
   for (int i = 0; i < T::BPW; ++i) {
     const int b = w + kWaves * i;
-    const int r = min(r0 + b + T::NB * slot, n - 1);
+    const int r = min(r0 + T::block_row(b, lane), n - 1);
     g2lds_16B(src + (long)r * D + 8 * chunk, dst + b * T::PITCH);
   }
 }
@@ -132,8 +184,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int B, int Hq, int Hkv,
     int Nq, int Nk, float c, float scale) {
   constexpr int BR = 32;  // query rows per tile
-  using T = RowTile<D, BR>;
-  using TV = RowTile<D, 128>;
+  using T = TrTile<D, BR>;      // Q, dO: read by rows and transposed
+  using TV = RowTile<D, 128>;   // V: read by rows only
   // the workgroup's 128 V rows, read as B operands every tile (holding
   // them in registers as well as K would leave one wave per SIMD)
   __shared__ __attribute__((aligned(16))) char v_lds[TV::BYTES];
@@ -182,8 +234,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
     kf[s] = *reinterpret_cast<const bf16x8*>(K + kvbase + (long)keyc * D + 16 * s + 8 * h);
-  load_tile<D, 128>(V + kvbase, k0, Nk, (lds_char*)v_lds, w, lane);
-  const lds_char* vrow = (const lds_char*)v_lds + TV::row_off(32 * w + r32) + 16 * h;
+  load_tile<D, TV>(V + kvbase, k0, Nk, (lds_char*)v_lds, w, lane);
+  const lds_char* vrow = (const lds_char*)v_lds + TV::row_off(32 * w + r32) + TV::chunk_off(h);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
@@ -200,8 +252,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const int g = it / per_head;
     const int t = t0 + (it - g * per_head);
     const long qb = (long)(ti.b * Hq + hk * G + g) * Nq;
-    load_tile<D, BR>(Q + qb * D, BR * t, Nq, qbuf(buf), w, lane);
-    load_tile<D, BR>(dO + qb * D, BR * t, Nq, obuf(buf), w, lane);
+    load_tile<D, T>(Q + qb * D, BR * t, Nq, qbuf(buf), w, lane);
+    load_tile<D, T>(dO + qb * D, BR * t, Nq, obuf(buf), w, lane);
     if (w == 0) {
       // the tile's 32 L2 values (lanes 0-31) then its 32 D values, one
       // dword per lane; rows past Nq read the next head's values or the
@@ -212,14 +264,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     }
   };
 
-  // per-lane fragment offsets in a tile: row r32 (+16 bytes for h); the
-  // transposed operand's rows 16j + 8e + 4h + i16/4 at column bytes
-  // 2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3))
-  // (row_off(r0 + x) = row_off(r0) + row_off(x) for the r0 used with x < 8,
-  // so each is one base register plus compile-time offsets)
-  const int rfrag = T::row_off(r32) + 16 * h;
+  // per-lane fragment offsets in a tile: row r32, chunk h (+ the step's
+  // chunks 2 sd); the transposed operand's rows 16j + 8e + 4h + i16/4 at
+  // column bytes 2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3)) (+ 64 mb).
+  // Each is one base register plus compile-time offsets (the layouts are
+  // additive over the splits used here).
+  const int rfrag = T::row_off(r32) + T::chunk_off(h);
   const int tbase = T::row_off(4 * h + (i16 >> 2)) +
-                    2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3));
+                    T::col_off(2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3)));
   auto tfrag = [&](int j, int e) { return tbase + T::row_off(16 * j + 8 * e); };
 
   constexpr std::integral_constant<int, 0> B0{};
@@ -248,8 +300,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     for (int v = 0; v < 16; ++v) s[v] = p[v] = 0.f;
 #pragma unroll
     for (int sd = 0; sd < D / 16; ++sd) {
-      s = mfma_32x32x16_bf16(lds_row16(qp + rfrag + 32 * sd), kf[sd], s);
-      p = mfma_32x32x16_bf16(lds_row16(op + rfrag + 32 * sd), lds_row16(vrow + 32 * sd), p);
+      s = mfma_32x32x16_bf16(lds_row16(qp + rfrag + T::chunk_off(2 * sd)), kf[sd], s);
+      p = mfma_32x32x16_bf16(lds_row16(op + rfrag + T::chunk_off(2 * sd)),
+                             lds_row16(vrow + TV::chunk_off(2 * sd)), p);
     }
     // P and dS per element; rows past Nq and causally hidden pairs get 0
     const lds_char* sp = sbuf(cur);
@@ -287,9 +340,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
         dv[mb] = mfma_32x32x16_bf16(
-            lds_tr16(op + tfrag(j, 0) + 64 * mb, op + tfrag(j, 1) + 64 * mb), pb, dv[mb]);
+            lds_tr16(op + tfrag(j, 0) + T::col_off(64 * mb),
+                     op + tfrag(j, 1) + T::col_off(64 * mb)), pb, dv[mb]);
         dk[mb] = mfma_32x32x16_bf16(
-            lds_tr16(qp + tfrag(j, 0) + 64 * mb, qp + tfrag(j, 1) + 64 * mb), db, dk[mb]);
+            lds_tr16(qp + tfrag(j, 0) + T::col_off(64 * mb),
+                     qp + tfrag(j, 1) + T::col_off(64 * mb)), db, dk[mb]);
       }
     }
   };
@@ -326,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     __bf16* __restrict__ dQ, int B, int Hq, int Hkv, int Nq, int Nk, float c,
     float scale) {
   constexpr int BN = 64;  // keys per tile
-  using T = RowTile<D, BN>;
+  using T = TrTile<D, BN>;  // K read by rows and transposed; V by rows
   __shared__ __attribute__((aligned(16))) char k_lds0[T::BYTES];
   __shared__ __attribute__((aligned(16))) char k_lds1[T::BYTES];
   __shared__ __attribute__((aligned(16))) char v_lds0[T::BYTES];
@@ -377,21 +432,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[mb][v] = 0.f;
 
-  // fragment offsets: K/V rows 32kb + r32 (+16 bytes for h); K^T rows
-  // 32kb + 16j + 8e + 4h + i16/4 at column bytes 2*(16*((lane>>4)&1) + 4*(i16&3))
-  // (row_off(r0 + x) = row_off(r0) + row_off(x) for the r0 used here, so
-  // each offset is one base register plus a compile-time constant)
-  const int rbase = T::row_off(r32) + 16 * h;
+  // fragment offsets: K/V rows 32kb + r32, chunk h (+ the step's chunks
+  // 2 sd); K^T rows 32kb + 16j + 8e + 4h + i16/4 at column bytes
+  // 2*(16*((lane>>4)&1) + 4*(i16&3)) (+ 64 mb). Each is one base register
+  // plus a compile-time constant (the layouts are additive over the splits
+  // used here).
+  const int rbase = T::row_off(r32) + T::chunk_off(h);
   const int tbase = T::row_off(4 * h + (i16 >> 2)) +
-                    2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3));
+                    T::col_off(2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3)));
   auto rfrag = [&](int kb) { return rbase + T::row_off(32 * kb); };
   auto tfrag = [&](int kb, int j, int e) {
     return tbase + T::row_off(32 * kb + 16 * j + 8 * e);
   };
 
   auto issue = [&](int tile, auto buf) {
-    load_tile<D, BN>(Kh, BN * tile, Nk, kbuf(buf), w, lane);
-    load_tile<D, BN>(Vh, BN * tile, Nk, vbuf(buf), w, lane);
+    load_tile<D, T>(Kh, BN * tile, Nk, kbuf(buf), w, lane);
+    load_tile<D, T>(Vh, BN * tile, Nk, vbuf(buf), w, lane);
   };
   auto skip_tile = [&](int tile) {
     return CAUSAL && (tile * BN > wrow0 + 31 + off);
@@ -422,8 +478,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     for (int sd = 0; sd < D / 16; ++sd)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma_32x32x16_bf16(lds_row16(kp + rfrag(kb) + 32 * sd), qf[sd], s[kb]);
-        p[kb] = mfma_32x32x16_bf16(lds_row16(vp + rfrag(kb) + 32 * sd), of[sd], p[kb]);
+        s[kb] = mfma_32x32x16_bf16(lds_row16(kp + rfrag(kb) + T::chunk_off(2 * sd)), qf[sd], s[kb]);
+        p[kb] = mfma_32x32x16_bf16(lds_row16(vp + rfrag(kb) + T::chunk_off(2 * sd)), of[sd], p[kb]);
       }
     const bool need_mask = (n0 + BN > Nk) || (CAUSAL && n0 + BN - 1 > wrow0 + off);
     const int lim = CAUSAL ? min(Nk - 1, row + off) : Nk - 1;
@@ -457,7 +513,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
           acc[mb] = mfma_32x32x16_bf16(
-              lds_tr16(kp + tfrag(kb, j, 0) + 64 * mb, kp + tfrag(kb, j, 1) + 64 * mb),
+              lds_tr16(kp + tfrag(kb, j, 0) + T::col_off(64 * mb),
+                       kp + tfrag(kb, j, 1) + T::col_off(64 * mb)),
               db, acc[mb]);
       }
   };
