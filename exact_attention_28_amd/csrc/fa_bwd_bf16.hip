@@ -242,15 +242,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
     for (int v = 0; v < 16; ++v) dk[mb][v] = dv[mb][v] = 0.f;
 
-  // query tiles [32t, 32t + 32) that can see a key of this workgroup
+  // query tiles [32t, 32t + 32) that can see a key of this workgroup,
+  // taken from the last one down, the group's heads inner: every workgroup
+  // of a KV head starts at the same tile and they move through Q and dO
+  // together, so a tile fetched once serves them from L2
   const int nqt = (Nq + BR - 1) / BR;
   const int t0 = CAUSAL ? min(nqt, max(0, k0 - off) / BR) : 0;
   const int per_head = nqt - t0;
   const int n_it = G * per_head;
 
   auto issue = [&](int it, auto buf) {
-    const int g = it / per_head;
-    const int t = t0 + (it - g * per_head);
+    const int g = it % G;
+    const int t = nqt - 1 - it / G;
     const long qb = (long)(ti.b * Hq + hk * G + g) * Nq;
     load_tile<D, T>(Q + qb * D, BR * t, Nq, qbuf(buf), w, lane);
     load_tile<D, T>(dO + qb * D, BR * t, Nq, obuf(buf), w, lane);
@@ -287,8 +290,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     wait_vm0();
     __syncthreads();
     if (it + 1 < n_it) issue(it + 1, nxt);
-    const int g = it / per_head;
-    const int t = t0 + (it - g * per_head);
+    const int g = it % G;
+    const int t = nqt - 1 - it / G;
     const int i0 = BR * t;
     (void)g;
     if (CAUSAL && i0 + BR - 1 + off < wk0) return;  // no row sees these keys
