@@ -34,21 +34,26 @@ constexpr int kThreads = 256;
 // ------------------------------------------------------------ LDS layout
 // A tile is 64 rows of D bytes, stored as 1 KB blocks (one direct load
 // instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B, so the 16-byte
-// units of equal block-relative offset rotate through the eight 16-byte
-// bank groups from block to block.
+// units of equal block-relative offset rotate through the sixteen 16-byte
+// bank groups (256 bytes of banks) from block to block.
 //  * K: block b holds rows b, b + NB, b + 2NB, ... The S^T = K Q^T A
 //    operand (32 bytes per lane: key 32kb + r32, bytes 64sd + 32h ..) is
-//    read as two 16-byte reads; the eight lanes served together hold eight
-//    consecutive keys, which sit in different blocks (D = 128) or in the
-//    same slot of four blocks and the next slot (D = 64): conflict free.
+//    read as two 16-byte reads; the sixteen lanes served together hold
+//    sixteen consecutive keys, which sit in eight blocks at two slots 128 B
+//    apart (D = 128) or four blocks at four slots 64 B apart (D = 64):
+//    conflict free.
 //  * V: read with ds_read_b64_tr_b8, which in each 16-lane group takes
 //    eight rows of 16 bytes (lane j names half j%2 of row j/2) and hands
 //    lane i byte i of every row. One read gives a lane 8 keys of its d
 //    column; the 8 keys of a read are k0..k0+3 and k0+8..k0+11 (the S^T
-//    accumulator order), and the layout puts them in eight different bank
-//    groups:
+//    accumulator order), in eight different blocks at one slot:
 //      D = 128: block (r%4) + 4((r/8)%2), slot (r/4)%2 + 2(r/16)
 //      D = 64:  block r%4, slot 8((r/4)%2) + r/8
+//    The two 16-lane groups of a 32-lane half read the same rows at the
+//    column chunks 2m and 2m + 1, so those must sit 128 B apart: the rows
+//    at slots s and s ^ S (S = 128 / D, the same block) trade pieces, and
+//    chunk 2m + q of the row whose slot is s is stored at slot s ^ (q S),
+//    16-byte position 2m + ((s / S) & 1) of that slot's row space.
 template <int D>
 struct Lay8 {
   static constexpr int RPB = 1024 / D;   // rows per 1 KB block
@@ -165,14 +170,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
       g2lds_16B(src + (long)min(k_row(w + 4 * i), last) * D,
                 dst + 4 * i * T::PITCH);
   };
+  // V: the piece this lane moves (see the layout above)
+  constexpr int kS = 128 / D;
+  const int vq = ((slot / kS) & 1) ^ (chunk & 1);
+  const int vslot = slot ^ (vq * kS);
+  const int vchunk = 2 * (chunk >> 1) + vq;
   auto issue_v = [&](int tile, auto buf) {
     const int n0 = tile * kBN;
-    const uint8_t* src = Vh + (long)n0 * D + 16 * chunk;
+    const uint8_t* src = Vh + (long)n0 * D + 16 * vchunk;
     lds_char* dst = vbuf(buf) + w * T::PITCH;
     const int last = min(kBN, Nk - n0) - 1;
 #pragma unroll
     for (int i = 0; i < T::BPW; ++i)
-      g2lds_16B(src + (long)min(v_row<D>(w + 4 * i, slot), last) * D,
+      g2lds_16B(src + (long)min(v_row<D>(w + 4 * i, vslot), last) * D,
                 dst + 4 * i * T::PITCH);
   };
 
@@ -202,15 +212,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   // order: byte t of 32 = key 32(t/16) + 8((t%16)/4) + 4h + t%4. Read j
   // (t = 8j..8j+7): this lane names row u = (r32%16)/2 of the read, i.e.
   // key 32(j/2) + 16(j%2) + 8(u/4) + 4h + u%4, bytes 16(r32/16) + 8(r32%2)
-  // of the 32-column block mb.
+  // of the 32-column block mb (chunk 2mb + r32/16, placed as above).
   int vaddr[4];
   {
     const int u = (r32 & 15) >> 1;
+    const int q = r32 >> 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = 32 * (j >> 1) + 16 * (j & 1) + 8 * (u >> 2) + 4 * h + (u & 3);
-      vaddr[j] = v_block<D>(key) * T::PITCH + v_slot<D>(key) * D +
-                 16 * (r32 >> 4) + 8 * (r32 & 1);
+      const int vs = v_slot<D>(key);
+      vaddr[j] = v_block<D>(key) * T::PITCH + (vs ^ (q * kS)) * D +
+                 16 * ((vs / kS) & 1) + 8 * (r32 & 1);
     }
   }
   auto skip_tile = [&](int tile) {
