@@ -120,10 +120,12 @@ __device__ __forceinline__ float add_e4m3x4(uint32_t w, float acc) {
 // One workgroup computes one BM-row query tile of one (batch, query head).
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2), so the block id is remapped to give every XCD a contiguous range of
-// logical tiles; logical order is (batch, kv head) group-major, so the
+// logical tiles; logical order is (kv head, batch) group-major, so the
 // query heads that share a KV head, and all their query tiles, run on one
-// XCD and hit the same K/V lines in its L2. Within a group, causal tiles go
-// heaviest (longest key range) first.
+// XCD and hit the same K/V lines in its L2, and the requests of a batch
+// (whose key ranges may differ, as in the paged cache) are spread over the
+// XCDs by KV head rather than handed out a few whole requests per XCD.
+// Within a group, causal tiles go heaviest (longest key range) first.
 struct TileIdx {
   int b, hq, qt;
 };
@@ -138,8 +140,8 @@ __device__ __forceinline__ TileIdx map_tile(int bid, int n_qt, int Hq,
   const int rem = lid - grp * per_group;
   const int rank = rem / G;
   TileIdx t;
-  t.b = grp / Hkv;
-  t.hq = (grp - t.b * Hkv) * G + (rem - rank * G);
+  t.b = grp % B;
+  t.hq = (grp / B) * G + (rem - rank * G);
   t.qt = causal ? (n_qt - 1 - rank) : rank;
   return t;
 }
