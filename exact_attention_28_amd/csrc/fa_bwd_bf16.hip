@@ -51,8 +51,9 @@ __device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // A row-major tile of ROWS rows x D bf16 in LDS, as 1 KB blocks (one direct
-// load instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B. Two layouts
-// with one interface: row_off(r) + chunk_off(k) is the byte offset of the
+// load instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B. RowTile
+// below and IlvTile (the interleaved layout, fa_device.h) share one
+// interface: row_off(r) + chunk_off(k) is the byte offset of the
 // 16-byte chunk k of row r, row_off(r) + col_off(x) that of byte x of row r,
 // and the direct load of block b moves chunk lane_chunk(lane) of row
 // block_row(b, lane) to byte 16 * lane of the block.
@@ -82,44 +83,9 @@ struct RowTile {
   static __device__ __forceinline__ int lane_chunk(int lane) { return lane % CPR; }
 };
 
-// IlvTile (d = 128, tiles read both by rows and transposed): block b holds
-// rows 4b .. 4b + 3 with their chunks interleaved in 64-byte groups: chunk
-// k = 4a + c of row 4b + j sits at byte 256a + 64j + 16c of the block.
-//  * row reads: sixteen consecutive rows at one chunk are four blocks x four
-//    rows; block b adds 16 b (mod 256) and row j adds 64 j, so the sixteen
-//    16-byte pieces cover the 256 bytes of the banks once;
-//  * transpose reads: a 32-lane half reads 64 contiguous bytes of each of
-//    four consecutive rows 4b .. 4b + 3, which sit 64 B apart: again each
-//    bank once.
-// Both offsets stay one per-lane base plus compile-time constants (row_off
-// is additive over multiples of 4 rows, chunk_off over the chunk's bit 0
-// and col_off over multiples of 64 bytes).
-template <int ROWS>
-struct IlvTile {
-  static constexpr int NB = ROWS / 4;
-  static constexpr int PITCH = 1040;
-  static constexpr int BYTES = NB * PITCH;
-  static constexpr int BPW = NB / kWaves;
-  static __device__ __forceinline__ constexpr int row_off(int r) {
-    return (r / 4) * PITCH + 64 * (r % 4);
-  }
-  static __device__ __forceinline__ constexpr int chunk_off(int k) {
-    return 256 * (k / 4) + 16 * (k % 4);
-  }
-  static __device__ __forceinline__ constexpr int col_off(int x) {
-    return 256 * (x / 64) + x % 64;
-  }
-  static __device__ __forceinline__ int block_row(int b, int lane) {
-    return 4 * b + ((lane >> 2) & 3);
-  }
-  static __device__ __forceinline__ int lane_chunk(int lane) {
-    return 4 * (lane >> 4) + (lane & 3);
-  }
-};
-
 // The layout of a tile that is read both ways.
 template <int D, int ROWS>
-using TrTile = std::conditional_t<D == 128, IlvTile<ROWS>, RowTile<D, ROWS>>;
+using TrTile = std::conditional_t<D == 128, IlvTile<ROWS, kWaves>, RowTile<D, ROWS>>;
 
 // Issues the direct loads of one tile of layout T: rows [r0, r0 + rows) of
 // a row-major [n, D] matrix, rows at or past n clamped to the last one

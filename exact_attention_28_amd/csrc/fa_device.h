@@ -116,6 +116,44 @@ __device__ __forceinline__ float add_e4m3x4(uint32_t w, float acc) {
   return acc + ((lo[0] + lo[1]) + (hi[0] + hi[1]));
 }
 
+// ------------------------------------------ interleaved LDS tile layout
+// A row-major tile of ROWS rows x 128 bf16 in LDS as 1 KB blocks (one
+// direct load instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B, for
+// tiles read by 16-byte rows and/or by the transpose read: block b holds
+// rows 4b .. 4b + 3 with their chunks interleaved in 64-byte groups: chunk
+// k = 4a + c of row 4b + j sits at byte 256a + 64j + 16c of the block.
+//  * row reads: sixteen consecutive rows at one chunk are four blocks x four
+//    rows; block b adds 16 b (mod 256) and row j adds 64 j, so the sixteen
+//    16-byte pieces cover the 256 bytes of the banks once;
+//  * transpose reads: a 32-lane half reads 64 contiguous bytes of each of
+//    four consecutive rows 4b .. 4b + 3, which sit 64 B apart: again each
+//    bank once.
+// Both offsets stay one per-lane base plus compile-time constants (row_off
+// is additive over multiples of 4 rows, chunk_off over the chunk's bit 0
+// and col_off over multiples of 64 bytes).
+template <int ROWS, int WAVES>
+struct IlvTile {
+  static constexpr int NB = ROWS / 4;
+  static constexpr int PITCH = 1040;
+  static constexpr int BYTES = NB * PITCH;
+  static constexpr int BPW = NB / WAVES;  // blocks each of WAVES waves loads
+  static __device__ __forceinline__ constexpr int row_off(int r) {
+    return (r / 4) * PITCH + 64 * (r % 4);
+  }
+  static __device__ __forceinline__ constexpr int chunk_off(int k) {
+    return 256 * (k / 4) + 16 * (k % 4);
+  }
+  static __device__ __forceinline__ constexpr int col_off(int x) {
+    return 256 * (x / 64) + x % 64;
+  }
+  static __device__ __forceinline__ int block_row(int b, int lane) {
+    return 4 * b + ((lane >> 2) & 3);
+  }
+  static __device__ __forceinline__ int lane_chunk(int lane) {
+    return 4 * (lane >> 4) + (lane & 3);
+  }
+};
+
 // ------------------------------------------------ workgroup -> tile map
 // One workgroup computes one BM-row query tile of one (batch, query head).
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own

@@ -46,19 +46,29 @@ struct Tile64 {
   static constexpr int PITCH = 1040;
   static constexpr int BYTES = NB * PITCH;
   static constexpr int BPW = NB / 4;
-  static __device__ __forceinline__ int row_off(int r) {
+  static __device__ __forceinline__ constexpr int row_off(int r) {
     return (r % NB) * PITCH + (r / NB) * (2 * D);
   }
+  static __device__ __forceinline__ constexpr int col_off(int x) { return x; }
+  static __device__ __forceinline__ int block_row(int b, int lane) {
+    return b + NB * (lane / CPR);
+  }
+  static __device__ __forceinline__ int lane_chunk(int lane) { return lane % CPR; }
 };
+// V tiles are only read transposed: at d = 128 the interleaved layout keeps
+// those reads conflict free (four consecutive rows 64 B apart)
 template <int D>
+using VTile64 = std::conditional_t<D == 128, IlvTile<64, 4>, Tile64<D>>;
+// Direct loads of rows [r0, r0 + 64) of a row-major [n, D] matrix into a
+// tile of layout T (rows past n clamped to the last one, never used).
+template <int D, class T = Tile64<D>>
 __device__ __forceinline__ void load64(const __bf16* src, int r0, int n,
                                        lds_char* dst, int w, int lane) {
-  using T = Tile64<D>;
-  const int slot = lane / T::CPR, chunk = lane % T::CPR;
+  const int chunk = T::lane_chunk(lane);
 #pragma unroll
   for (int i = 0; i < T::BPW; ++i) {
     const int b = w + 4 * i;
-    const int r = min(r0 + b + T::NB * slot, n - 1);
+    const int r = min(r0 + T::block_row(b, lane), n - 1);
     g2lds_16B(src + (long)r * D + 8 * chunk, dst + b * T::PITCH);
   }
 }
@@ -188,7 +198,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void naive_pv_kernel(
     const __bf16* __restrict__ P, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, int B, int Hq, int Hkv, int Nq, int Nk) {
-  using T = Tile64<D>;
+  using T = VTile64<D>;
   __shared__ __attribute__((aligned(16))) char vl0[T::BYTES];
   __shared__ __attribute__((aligned(16))) char vl1[T::BYTES];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -209,14 +219,14 @@ __global__ __launch_bounds__(kThreads, 2) void naive_pv_kernel(
   // transposed read offsets: rows 16j + 8e + 4h + i16/4 of the tile,
   // columns 2*(16*((lane>>4)&1) + 4*(i16&3)) bytes (+64 per 32 columns)
   const int tbase = T::row_off(4 * h + (i16 >> 2)) +
-                    2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3));
+                    T::col_off(2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3)));
   auto buf = [&](int i) -> lds_char* { return (lds_char*)(i ? vl1 : vl0); };
   const int nt = (Nk + 63) / 64;
-  load64<D>(Vh, 0, Nk, buf(0), w, lane);
+  load64<D, T>(Vh, 0, Nk, buf(0), w, lane);
   for (int t = 0; t < nt; ++t) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (t + 1 < nt) load64<D>(Vh, 64 * (t + 1), Nk, buf((t + 1) & 1), w, lane);
+    if (t + 1 < nt) load64<D, T>(Vh, 64 * (t + 1), Nk, buf((t + 1) & 1), w, lane);
     const lds_char* vp = buf(t & 1);
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {  // 16-key steps of the tile
@@ -241,9 +251,9 @@ __global__ __launch_bounds__(kThreads, 2) void naive_pv_kernel(
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
         const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(vp + tbase + rl + 64 * mb));
+            (lds_bf16x4*)(vp + tbase + rl + T::col_off(64 * mb)));
         const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(vp + tbase + rh + 64 * mb));
+            (lds_bf16x4*)(vp + tbase + rh + T::col_off(64 * mb)));
         const bf16x8 av = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         o[mb] = mfma_32x32x16_bf16(av, pb, o[mb]);
       }
