@@ -55,8 +55,8 @@ def _run(fa, B, Hq, Hkv, Nq, Nk, d, causal, seed):
     return out, ref
 
 
-def _check(out, ref, what):
-    for name, a, r in zip(("dQ", "dK", "dV"), out, ref):
+def _check(out, ref, what, names=("dQ", "dK", "dV")):
+    for name, a, r in zip(names, out, ref):
         assert not np.any(np.isnan(a)), f"{what} {name} NaN"
         err = float(np.max(np.abs(a - r)))
         bound = RTOL * float(np.max(np.abs(r))) + ATOL
@@ -121,3 +121,39 @@ def test_backward_long_causal_sampled(fa):
            dk.double().cpu().numpy()[:, :, N - n:],
            dv.double().cpu().numpy()[:, :, N - n:]]
     _check(out, (dq_ref, dk_ref, dv_ref), "long causal corner")
+
+
+def test_backward_full_workload_sampled(fa):
+    # the causal GQA prefill at full size (B=1, Hq=32, Hkv=8, N=16384,
+    # d=128, the shape and launch the benchmark times), dO from seed 43:
+    # dQ of the first, a middle and the last 64 rows, each against the
+    # oracle on the key prefix those rows can see (so the bottom-right
+    # alignment of the sliced problem is the true one), and dK, dV of the
+    # last 64 keys, which only the last 64 rows see
+    name = "bf16_causal_gqa_b1_hq32_hkv8_n16384_d128"
+    c = W.PREFILL_CONFIGS[name]
+    inp = W.prefill_config(name)
+    N = c["Nq"]
+    g = W.upstream_grad(tuple(inp.q.shape), seed=43)
+    dev = torch.device("cuda:0")
+    print(f"bwd full workload {name}", flush=True)
+    q, k, v, do = (t.to(dev) for t in (inp.q, inp.k, inp.v, g))
+    o, lse = fa.attention(q, k, v, causal=True, scale=inp.scale)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, causal=True,
+                                       scale=inp.scale)
+    torch.cuda.synchronize()
+    dq = dq.double().cpu().numpy()
+    dk = dk.double().cpu().numpy()
+    dv = dv.double().cpu().numpy()
+    q64, k64, v64, g64 = (W.as_f64(t) for t in (inp.q, inp.k, inp.v, g))
+    n = 64
+    for r0 in (0, N // 2 + 37, N - n):
+        ref = oracle.attention_backward(q64[:, :, r0:r0 + n],
+                                        k64[:, :, :r0 + n], v64[:, :, :r0 + n],
+                                        g64[:, :, r0:r0 + n], inp.scale,
+                                        causal=True)
+        _check([dq[:, :, r0:r0 + n]], [ref[0]], f"full workload dQ rows {r0}..")
+        if r0 == N - n:
+            _check([dk[:, :, r0:], dv[:, :, r0:]],
+                   [ref[1][:, :, r0:], ref[2][:, :, r0:]],
+                   "full workload dK, dV of the last keys", names=("dK", "dV"))
