@@ -77,6 +77,7 @@ struct PagedKV {
   int max_pages, num_pages;
 };
 constexpr int kMaxPagesLds = 8192;  // page-table entries a workgroup stages
+constexpr int kMaxRankB = 256;      // batches up to this size run longest first
 
 template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
@@ -114,7 +115,31 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   const TileIdx ti = map_tile(blockIdx.x, n_qt, Hq, Hkv, B, CAUSAL);
   const int hk = ti.hq / (Hq / Hkv);
   const int q0 = ti.qt * kBM;
-  const long qbase = (long)(ti.b * Hq + ti.hq) * Nq * D;
+  // The batch index this workgroup serves. For the paged cache, whose
+  // requests differ in length, the logical index is a rank: requests are
+  // taken longest first (ties by index), so the longest workgroups start
+  // first and the grid ends without a ragged tail. Each workgroup ranks the
+  // lengths itself (a batch of at most kMaxRankB requests; larger batches
+  // keep their order).
+  int bq = ti.b;
+  if constexpr (PAGED) {
+    if (B <= kMaxRankB) {
+      __shared__ int ranked;
+      const int cap = pk.max_pages * 16;
+      for (int r = tid; r < B; r += kThreads) {
+        const int lr = max(0, min(pk.sl[r], cap));
+        int rank = 0;
+        for (int r2 = 0; r2 < B; ++r2) {
+          const int l2 = max(0, min(pk.sl[r2], cap));
+          rank += (l2 > lr) || (l2 == lr && r2 < r);
+        }
+        if (rank == ti.b) ranked = r;
+      }
+      __syncthreads();
+      bq = ranked;
+    }
+  }
+  const long qbase = (long)(bq * Hq + ti.hq) * Nq * D;
   // keys of this request; for the paged cache its length, and the page
   // table staged in LDS (ids outside the pool are replaced by 0 and turn
   // the request's output to NaN)
@@ -122,13 +147,13 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   __shared__ int page_bad;
   int nk = Nk;
   if constexpr (PAGED) {
-    nk = max(0, min(pk.sl[ti.b], pk.max_pages * 16));
+    nk = max(0, min(pk.sl[bq], pk.max_pages * 16));
     const int np = (nk + 15) / 16;
     if (tid == 0) page_bad = 0;
     __syncthreads();
     bool bad = false;
     for (int i = tid; i < np; i += kThreads) {
-      const int id = pk.bt[(long)ti.b * pk.max_pages + i];
+      const int id = pk.bt[(long)bq * pk.max_pages + i];
       const bool ok = id >= 0 && id < pk.num_pages;
       page_ids[i] = ok ? id : 0;
       bad |= !ok;
@@ -138,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   }
   // contiguous: the head's K/V; paged: the pool plus this head's offset
   // within a token row (rows of a page are Hkv * d apart)
-  const long kv_head = PAGED ? (long)hk * D : (long)(ti.b * Hkv + hk) * Nk * D;
+  const long kv_head = PAGED ? (long)hk * D : (long)(bq * Hkv + hk) * Nk * D;
   const __bf16* Kh = K + kv_head;
   const __bf16* Vh = V + kv_head;
   const long tok_stride = PAGED ? (long)Hkv * D : D;
@@ -383,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
         *reinterpret_cast<u32x2*>(orow + 32 * mb + 8 * g + 4 * h) = pr;
       }
     if (h == 0 && LSE != nullptr)
-      LSE[(long)(ti.b * Hq + ti.hq) * Nq + row] =
+      LSE[(long)(bq * Hq + ti.hq) * Nq + row] =
           nan_out ? __builtin_nanf("")
                   : (live ? (st.m + fast_log2(ltot)) * kLn2 : kNegInf);
   }
