@@ -364,8 +364,10 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
         }
       __builtin_amdgcn_s_setprio(0);
     }
-    // tile t+1 needs K(t+2) and V(t+1); with three V buffers the V(t+2)
-    // loads just issued (the last BPW in flight) may still be pending
+    // tile t+1 needs K(t+2) and V(t+1), so only the V(t+2) loads just
+    // issued (the last BPW in flight) could stay pending; the barrier's
+    // workgroup fence then waits for the wave's remaining direct loads as
+    // well, so every load has this tile's compute time to land
     if (kVStages > 2 && more_v) __builtin_amdgcn_s_waitcnt(0x0F70 | T::BPW);
     else wait_vm0();
     __syncthreads();
