@@ -432,6 +432,20 @@ def test_paged_prefill_matches_oracle(fa, d, hq, hkv, nq, causal):
              f"paged prefill d{d} {hq}/{hkv} Nq={nq} causal={causal}")
 
 
+def test_paged_prefill_equal_lengths_keep_their_requests(fa):
+    # the kernel takes requests longest first, ties by index: requests of
+    # equal length (and an empty one) must still each get their own output
+    lens = [300, 5, 300, 0, 300, 64]
+    di = W.paged_prefill_inputs(len(lens), 8, 2, 128, 40, lens=lens,
+                                max_pages=20, seed=23, extra_pages=2)
+    o, lse = _gpu_paged_prefill(fa, di, True)
+    ro, rl = oracle.paged_prefill(W.as_f64(di.q), W.as_f64(di.k_pool),
+                                  W.as_f64(di.v_pool), di.block_table.numpy(),
+                                  di.seq_lens.numpy(), di.page_size, di.scale,
+                                  causal=True)
+    _compare(o, lse, ro, rl, "bf16", "paged prefill, equal lengths")
+
+
 def test_paged_prefill_bad_page_gives_nan(fa):
     di = W.paged_prefill_inputs(3, 8, 2, 128, 32, lens=[100, 100, 100],
                                 max_pages=8, seed=4)
