@@ -254,12 +254,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
       if constexpr (!KV8) {
         kf = pr_in.k[s];
       } else {
-        float f[8];
-        e4m3x4_to_f32(pr_in.k[s / 2][2 * (s & 1)], f);
-        e4m3x4_to_f32(pr_in.k[s / 2][2 * (s & 1) + 1], f + 4);
-        const u32x4 w = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                         pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
-        kf = __builtin_bit_cast(bf16x8, w);
+        // e4m3 pairs straight to bf16 pairs (exact: scale 1, 3 -> 7
+        // mantissa bits)
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const int w0 = (int)pr_in.k[s / 2][2 * (s & 1)];
+        const int w1 = (int)pr_in.k[s / 2][2 * (s & 1) + 1];
+        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false);
+        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true);
+        const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false);
+        const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true);
+        kf = bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
       }
       acc = mfma_16x16x32_bf16(kf, qf[s], acc);
     }
