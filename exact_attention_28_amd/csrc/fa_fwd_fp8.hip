@@ -278,6 +278,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
       // S(t+1) on the matrix cores while P(t) is formed on the VALU (past
       // the last tile, or beyond this wave's causal rows, the product is
       // never read and its buffer is not being written)
+      // raised issue priority while this wave feeds the matrix cores: the
+      // other wave of the SIMD fills in with its VALU work
+      __builtin_amdgcn_s_setprio(1);
       qk(nxt, sn);
       const float mref = (st.m == kNegInf) ? 0.f : st.m;
       float sum = 0.f;
@@ -309,6 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         }
         o[mb] = mfma_32x32x64_e4m3(a, pb, o[mb]);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     wait_vm0();
     __syncthreads();
