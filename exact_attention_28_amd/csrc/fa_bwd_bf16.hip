@@ -263,16 +263,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     if (CAUSAL && i0 + BR - 1 + off < wk0) return;  // no row sees these keys
     const lds_char* qp = qbuf(cur);
     const lds_char* op = obuf(cur);
-    // S = Q K^T and dP = dO V^T: lane = key r32, rows 8(v/4) + 4h + v%4
+    // S = Q K^T and dP = dO V^T: lane = key r32, rows 8(v/4) + 4h + v%4.
+    // The MFMA phases run at raised issue priority, so while one wave
+    // feeds the matrix cores the other wave of the SIMD fills in with its
+    // VALU work.
     f32x16 s, p;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = p[v] = 0.f;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int sd = 0; sd < D / 16; ++sd) {
       s = mfma_32x32x16_bf16(lds_row16(qp + rfrag + T::chunk_off(2 * sd)), kf[sd], s);
       p = mfma_32x32x16_bf16(lds_row16(op + rfrag + T::chunk_off(2 * sd)),
                              lds_row16(vrow + TV::chunk_off(2 * sd)), p);
     }
+    __builtin_amdgcn_s_setprio(0);
     // P and dS per element; rows past Nq and causally hidden pairs get 0
     const lds_char* sp = sbuf(cur);
     const bool need_mask = (i0 + BR > Nq) || (CAUSAL && i0 + off < wk0 + 31);
@@ -302,6 +307,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       dd[j][t2 + 1] = pack_bf16x2(dv4[2], dv4[3]);
     }
     // dV^T += dO^T P and dK^T += Q^T dS, 16 rows per MFMA
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pp[j][0], pp[j][1], pp[j][2], pp[j][3]});
@@ -316,6 +322,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                      qp + tfrag(j, 1) + T::col_off(64 * mb)), db, dk[mb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   for (int it = 0; it < n_it; it += 2) {
     step(it, B0);
@@ -443,6 +450,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kb][v] = p[kb][v] = 0.f;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int sd = 0; sd < D / 16; ++sd)
 #pragma unroll
@@ -450,6 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         s[kb] = mfma_32x32x16_bf16(lds_row16(kp + rfrag(kb) + T::chunk_off(2 * sd)), qf[sd], s[kb]);
         p[kb] = mfma_32x32x16_bf16(lds_row16(vp + rfrag(kb) + T::chunk_off(2 * sd)), of[sd], p[kb]);
       }
+    __builtin_amdgcn_s_setprio(0);
     const bool need_mask = (n0 + BN > Nk) || (CAUSAL && n0 + BN - 1 > wrow0 + off);
     const int lim = CAUSAL ? min(Nk - 1, row + off) : Nk - 1;
     uint32_t dd[2][2][4];
@@ -473,6 +482,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
           dd[kb][j][t2] = pack_bf16x2(ds[8 * j + 2 * t2], ds[8 * j + 2 * t2 + 1]);
     }
     // dQ^T += K^T dS^T, 16 keys per MFMA
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -486,6 +496,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                        kp + tfrag(kb, j, 1) + T::col_off(64 * mb)),
               db, acc[mb]);
       }
+    __builtin_amdgcn_s_setprio(0);
   };
   for (int t = 0; t < nt; t += 2) {
     step(t, B0);
