@@ -78,6 +78,7 @@ struct PagedKV {
 };
 constexpr int kMaxPagesLds = 8192;  // page-table entries a workgroup stages
 constexpr int kMaxRankB = 256;      // batches up to this size run longest first
+static_assert(kMaxRankB <= kThreads, "one request length per thread");
 
 template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
@@ -124,16 +125,19 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   int bq = ti.b;
   if constexpr (PAGED) {
     if (B <= kMaxRankB) {
+      __shared__ int lens[kMaxRankB];
       __shared__ int ranked;
       const int cap = pk.max_pages * 16;
-      for (int r = tid; r < B; r += kThreads) {
-        const int lr = max(0, min(pk.sl[r], cap));
+      if (tid < B) lens[tid] = max(0, min(pk.sl[tid], cap));
+      __syncthreads();
+      if (tid < B) {
+        const int lr = lens[tid];
         int rank = 0;
         for (int r2 = 0; r2 < B; ++r2) {
-          const int l2 = max(0, min(pk.sl[r2], cap));
-          rank += (l2 > lr) || (l2 == lr && r2 < r);
+          const int l2 = lens[r2];
+          rank += (l2 > lr) || (l2 == lr && r2 < tid);
         }
-        if (rank == ti.b) ranked = r;
+        if (rank == ti.b) ranked = tid;
       }
       __syncthreads();
       bq = ranked;
