@@ -1,9 +1,10 @@
 /*
  * fa.h - C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
  *
- * Two operations, both exact attention O = softmax(scale * Q K^T) V computed
- * in one streaming pass with an online softmax, so the score matrix S and
- * the probability matrix P never reach device memory:
+ * Exact attention O = softmax(scale * Q K^T) V, computed in one streaming
+ * pass with an online softmax so that the score matrix S and the
+ * probability matrix P never reach device memory, in the forms below (the
+ * last one, the unfused contrast, is the exception and writes both):
  *
  *   fa_fwd           prefill / training forward over contiguous Q, K, V.
  *   fa_bwd           training backward: dQ, dK, dV from the forward's O and
@@ -38,7 +39,10 @@
  *   state between calls: calls from several host threads are safe.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *   stream) and runs asynchronously: outputs are valid once the stream has
- *   reached the call. Nothing inside synchronises with the host.
+ *   reached the call. Nothing inside synchronises with the host, allocates
+ *   or records a memset, so the calls may be captured into a HIP graph
+ *   (replays read the captured pointers; workspace contents on entry never
+ *   matter).
  * - Inputs are read-only. Outputs are fully overwritten.
  * - Return value: FA_OK (0) on success. A negative FA_E* code means the
  *   arguments were rejected before anything was launched and nothing was
