@@ -30,6 +30,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
@@ -188,6 +189,63 @@ __global__ __launch_bounds__(kThreads) void naive_softmax_kernel(
   if (tid == 0 && LSE != nullptr) LSE[rowid] = l > 0.f ? m + __logf(l) : kNegInf;
 }
 
+// The same softmax with one wave per row (rows of up to 4096 keys): the
+// row is read as 16-byte pieces of 8 scores (Nk is a multiple of 8, so rows
+// are 16-byte aligned), max and sum are reduced inside the wave by lane
+// exchanges (no barrier), and P goes back as 16-byte pieces. This keeps the
+// kernel a plain stream of S in and P out.
+template <int NC>  // 8-score pieces per lane: NC * 512 >= Nk
+__global__ __launch_bounds__(kThreads) void naive_softmax_wave_kernel(
+    _Float16* __restrict__ S, float* __restrict__ LSE, long rows, int Nq,
+    int Nk, bool causal) {
+  const int lane = threadIdx.x & 63;
+  const long rowid = (long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (rowid >= rows) return;
+  const int i = (int)(rowid % Nq);
+  const int lim = causal ? min(Nk, i + (Nk - Nq) + 1) : Nk;  // visible keys
+  _Float16* srow = S + rowid * Nk;
+  float x[NC][8];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int j0 = 8 * (lane + 64 * c);
+    f16x8 v8 = {};
+    if (j0 < Nk) v8 = *reinterpret_cast<const f16x8*>(srow + j0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[c][e] = (j0 + e < lim) ? (float)v8[e] : kNegInf;
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, x[c][e]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float mref = (m == kNegInf) ? 0.f : m;
+  float l = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[c][e] = fast_exp2((x[c][e] - mref) * kLog2e);
+      l += x[c][e];
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  __bf16* prow = reinterpret_cast<__bf16*>(srow);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int j0 = 8 * (lane + 64 * c);
+    if (j0 < Nk) {
+      bf16x8 p8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p8[e] = (__bf16)(x[c][e] * inv);
+      *reinterpret_cast<bf16x8*>(prow + j0) = p8;
+    }
+  }
+  if (lane == 0 && LSE != nullptr) LSE[rowid] = l > 0.f ? m + __logf(l) : kNegInf;
+}
+
 // ----------------------------------------------------------- O = P V
 // Workgroup: 128 rows (32 per wave) of one (batch, head); V streams through
 // LDS in 64-key tiles and is read transposed (ds_read_b64_tr_b16) as the A
@@ -285,7 +343,21 @@ hipError_t launch(const NaiveArgs& a) {
   if (e != hipSuccess) return e;
   const unsigned rows = (unsigned)((long)a.B * a.Hq * a.Nq);
   const int nv = (a.Nk + kThreads - 1) / kThreads;
-  if (nv <= 8)
+  const int nc = (a.Nk + 511) / 512;
+  const unsigned wgrid = (rows + kThreads / 64 - 1) / (kThreads / 64);
+  if (nc <= 1)
+    hipLaunchKernelGGL((naive_softmax_wave_kernel<1>), dim3(wgrid), dim3(kThreads), 0,
+                       a.stream, S, a.lse, (long)rows, a.Nq, a.Nk, a.causal);
+  else if (nc <= 2)
+    hipLaunchKernelGGL((naive_softmax_wave_kernel<2>), dim3(wgrid), dim3(kThreads), 0,
+                       a.stream, S, a.lse, (long)rows, a.Nq, a.Nk, a.causal);
+  else if (nc <= 4)
+    hipLaunchKernelGGL((naive_softmax_wave_kernel<4>), dim3(wgrid), dim3(kThreads), 0,
+                       a.stream, S, a.lse, (long)rows, a.Nq, a.Nk, a.causal);
+  else if (nc <= 8)
+    hipLaunchKernelGGL((naive_softmax_wave_kernel<8>), dim3(wgrid), dim3(kThreads), 0,
+                       a.stream, S, a.lse, (long)rows, a.Nq, a.Nk, a.causal);
+  else if (nv <= 8)
     hipLaunchKernelGGL((naive_softmax_kernel<8>), dim3(rows), dim3(kThreads), 0,
                        a.stream, S, a.lse, a.Nq, a.Nk, a.causal);
   else if (nv <= 16)

@@ -386,6 +386,10 @@ def _gpu_naive(fa, inp):
     (1, 4, 2, 200, 200, 128, True),
     (2, 2, 1, 130, 96, 64, True),       # Nq > Nk: early rows see no key
     (1, 2, 2, 77, 304, 64, False),
+    (1, 2, 1, 48, 1496, 128, False),    # several 8-score pieces per lane,
+                                        # the last lanes' pieces past Nk
+    (1, 2, 2, 64, 2048, 128, True),     # the benchmark's row length
+    (1, 2, 2, 40, 4104, 64, True),      # past one wave per row
 ])
 def test_naive_matches_oracle(fa, B, Hq, Hkv, Nq, Nk, d, causal):
     inp = W.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", causal=causal,
