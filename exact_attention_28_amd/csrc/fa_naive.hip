@@ -78,7 +78,9 @@ __device__ __forceinline__ void load64(const __bf16* src, int r0, int n,
 // Workgroup: 128 query rows (32 per wave) of one (batch, head) against
 // every key, 64 keys per tile. S = Q K^T with Q as the A operand (rows in
 // registers) and K^T as the B operand (key rows from LDS), so a lane holds
-// one key column and consecutive lanes write consecutive keys of a row.
+// one key column. Each wave's 32 x 64 tile of S goes through a small LDS
+// buffer (row pitch 136 B) and leaves as 16-byte pieces, eight lanes per
+// 128-byte row segment, so the stores of S are whole segments.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void naive_scores_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -87,6 +89,8 @@ __global__ __launch_bounds__(kThreads, 2) void naive_scores_kernel(
   using T = Tile64<D>;
   __shared__ __attribute__((aligned(16))) char kl0[T::BYTES];
   __shared__ __attribute__((aligned(16))) char kl1[T::BYTES];
+  constexpr int kSPitch = 136;  // bytes per staged row of 64 fp16 scores
+  __shared__ __attribute__((aligned(16))) char sl[4][32 * kSPitch];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int h = lane >> 5, r32 = lane & 31;
   const int n_qt = (Nq + 127) / 128;
@@ -118,15 +122,24 @@ __global__ __launch_bounds__(kThreads, 2) void naive_scores_kernel(
       for (int s = 0; s < D / 16; ++s)
         acc = mfma_32x32x16_bf16(
             qa[s], *(const lds_bf16x8*)(kp + kfrag + T::row_off(32 * kb) + 32 * s), acc);
-      // lane: key 64t + 32kb + r32, rows 8(v/4) + 4h + v%4 of the wave's 32
-      const int key = 64 * t + 32 * kb + r32;
-      if (key < Nk) {
+      // lane: key 32kb + r32 of the tile, rows 8(v/4) + 4h + v%4
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = row0 + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (row < Nq) S[(bh * Nq + row) * Nk + key] = (_Float16)(acc[v] * scale);
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+        *(__attribute__((address_space(3))) _Float16*)(
+            (lds_char*)sl[w] + r * kSPitch + 2 * (32 * kb + r32)) =
+            (_Float16)(acc[v] * scale);
       }
+    }
+    // the wave's tile back out: lane l takes 8 keys (16 B) of row l/8 + 8i
+    const int chunk = lane & 7, key = 64 * t + 8 * chunk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (lane >> 3) + 8 * i;
+      const u32x4 piece = *(const __attribute__((address_space(3))) u32x4*)(
+          (lds_char*)sl[w] + r * kSPitch + 16 * chunk);
+      if (key < Nk && row0 + r < Nq)
+        *reinterpret_cast<u32x4*>(S + (bh * Nq + row0 + r) * Nk + key) = piece;
     }
   }
 }
@@ -249,16 +262,23 @@ __global__ __launch_bounds__(kThreads) void naive_softmax_wave_kernel(
 // ----------------------------------------------------------- O = P V
 // Workgroup: 128 rows (32 per wave) of one (batch, head); V streams through
 // LDS in 64-key tiles and is read transposed (ds_read_b64_tr_b16) as the A
-// operand of O^T = V^T P^T; P^T's B operand comes straight from the P rows
-// in HBM (lane: row r32, keys 16j + 4h + 0..3 and + 8, the order the
-// transposed V read delivers).
+// operand of O^T = V^T P^T. Each wave's 32 x 64 tile of P comes in by
+// direct loads too (whole 128-byte row segments), into four 1 KB blocks at
+// a 1032-byte pitch: block b holds rows 8b .. 8b + 7, the 8-byte unit u of
+// row 8b + j at unit 32 (u / 4) + 4 j + u % 4 of the block, so the P^T B
+// operand (lane: row r32, keys 16j + 4h + 0..3 and + 8, the order the
+// transposed V read delivers) is two 8-byte reads that meet no bank
+// conflict.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void naive_pv_kernel(
     const __bf16* __restrict__ P, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, int B, int Hq, int Hkv, int Nq, int Nk) {
   using T = VTile64<D>;
+  constexpr int kPPitch = 1032;
   __shared__ __attribute__((aligned(16))) char vl0[T::BYTES];
   __shared__ __attribute__((aligned(16))) char vl1[T::BYTES];
+  __shared__ __attribute__((aligned(16))) char pl0[4][4 * kPPitch];
+  __shared__ __attribute__((aligned(16))) char pl1[4][4 * kPPitch];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int h = lane >> 5, r32 = lane & 31, i16 = lane & 15;
   const int n_qt = (Nq + 127) / 128;
@@ -266,9 +286,8 @@ __global__ __launch_bounds__(kThreads, 2) void naive_pv_kernel(
   const int hk = ti.hq / (Hq / Hkv);
   const long bh = (long)ti.b * Hq + ti.hq;
   const __bf16* Vh = V + ((long)ti.b * Hkv + hk) * Nk * D;
-  const int row = ti.qt * 128 + 32 * w + r32;
-  const int rowc = min(row, Nq - 1);
-  const __bf16* prow = P + (bh * Nq + rowc) * Nk;
+  const int row0 = ti.qt * 128 + 32 * w;
+  const int row = row0 + r32;
   f32x16 o[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
@@ -279,31 +298,40 @@ __global__ __launch_bounds__(kThreads, 2) void naive_pv_kernel(
   const int tbase = T::row_off(4 * h + (i16 >> 2)) +
                     T::col_off(2 * (16 * ((lane >> 4) & 1) + 4 * (i16 & 3)));
   auto buf = [&](int i) -> lds_char* { return (lds_char*)(i ? vl1 : vl0); };
+  auto pbuf = [&](int i) -> lds_char* { return (lds_char*)(i ? pl1[w] : pl0[w]); };
+  // this lane's piece of the P tile: row 8b + (lane%16)/2, keys 8c .. 8c+7
+  // with c = 2 (lane/16) + lane%2 (rows past Nq and keys past Nk are read
+  // from a clamped place; their P is replaced by 0 below)
+  const int pj = (lane & 15) >> 1, pc = 2 * (lane >> 4) + (lane & 1);
+  auto load_p = [&](int tile, lds_char* dst) {
+    const int key = min(64 * tile + 8 * pc, Nk - 8);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r = min(row0 + 8 * b + pj, Nq - 1);
+      g2lds_16B(P + (bh * Nq + r) * Nk + key, dst + b * kPPitch);
+    }
+  };
+  const int pfrag = (r32 >> 3) * kPPitch + 32 * (r32 & 7) + 8 * h;
   const int nt = (Nk + 63) / 64;
   load64<D, T>(Vh, 0, Nk, buf(0), w, lane);
+  load_p(0, pbuf(0));
   for (int t = 0; t < nt; ++t) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (t + 1 < nt) load64<D, T>(Vh, 64 * (t + 1), Nk, buf((t + 1) & 1), w, lane);
+    if (t + 1 < nt) {
+      load64<D, T>(Vh, 64 * (t + 1), Nk, buf((t + 1) & 1), w, lane);
+      load_p(t + 1, pbuf((t + 1) & 1));
+    }
     const lds_char* vp = buf(t & 1);
+    const lds_char* pp = pbuf(t & 1) + pfrag;
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {  // 16-key steps of the tile
       const int k0 = 64 * t + 16 * j4 + 4 * h;
-      u32x2 lo = {0u, 0u}, hi = {0u, 0u};
-      if (k0 + 4 <= Nk) lo = *reinterpret_cast<const u32x2*>(prow + k0);
-      else
-        for (int e = 0; e < 4; ++e)
-          if (k0 + e < Nk) {
-            const uint16_t bits = reinterpret_cast<const uint16_t*>(prow)[k0 + e];
-            lo[e / 2] |= (uint32_t)bits << (16 * (e & 1));
-          }
-      if (k0 + 12 <= Nk) hi = *reinterpret_cast<const u32x2*>(prow + k0 + 8);
-      else
-        for (int e = 0; e < 4; ++e)
-          if (k0 + 8 + e < Nk) {
-            const uint16_t bits = reinterpret_cast<const uint16_t*>(prow)[k0 + 8 + e];
-            hi[e / 2] |= (uint32_t)bits << (16 * (e & 1));
-          }
+      u32x2 lo = *(const __attribute__((address_space(3))) u32x2*)(pp + 256 * j4);
+      u32x2 hi = *(const __attribute__((address_space(3))) u32x2*)(pp + 256 * j4 + 16);
+      // keys past Nk (the ragged last tile; Nk is a multiple of 8) weigh 0
+      if (k0 >= Nk) lo = u32x2{0u, 0u};
+      if (k0 + 8 >= Nk) hi = u32x2{0u, 0u};
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
       const int rl = T::row_off(16 * j4), rh = T::row_off(16 * j4 + 8);
 #pragma unroll
