@@ -82,6 +82,7 @@ SHAPES = [
     (1, 4, 4, 1000, 1000),
     (1, 2, 2, 300, 1000),
     (1, 2, 1, 1000, 300),
+    (3, 6, 2, 150, 200),    # odd group size; a tile count not divisible by 8
 ]
 
 
