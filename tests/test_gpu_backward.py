@@ -74,6 +74,7 @@ def _check(out, ref, what, names=("dQ", "dK", "dV")):
     (1, 2, 1, 96, 300, 128, True),       # Nk > Nq (bottom-right causal)
     (1, 2, 2, 300, 96, 128, True),       # Nq > Nk: early rows see no key
     (1, 2, 2, 333, 257, 64, False),
+    (3, 6, 2, 150, 200, 128, True),      # odd group size, B = 3
 ])
 def test_backward_matches_oracle(fa, B, Hq, Hkv, Nq, Nk, d, causal):
     out, ref = _run(fa, B, Hq, Hkv, Nq, Nk, d, causal, seed=Nq + Nk + d)
