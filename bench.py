@@ -73,6 +73,13 @@ def decode_bytes(di, Hkv, d, kv_elem_bytes=2):
     return kv + B * Hq * d * 2 * 2 + B * Hq * 4 + pages * 4
 
 
+def _launch_stats(samples):
+    """Mean, median, min and max of one leg's per-launch times in ms."""
+    return {"launch_ms_mean": statistics.mean(samples),
+            "launch_ms_median": statistics.median(samples),
+            "launch_ms_min": min(samples), "launch_ms_max": max(samples)}
+
+
 def _src_hash(names):
     h = hashlib.sha256()
     for n in names:
@@ -361,9 +368,10 @@ def main():
             "traffic": _traffic("fwd_bf16_causal_n16384",
                                 ["fa_fwd_bf16.hip", "fa_device.h"]),
             "algorithmic_gflop_per_launch": info["prefill"]["flops"] / 1e9,
-            "launch_ms_mean": t * 1e3,
-            "launch_ms_min": min(ms["prefill"]),
-            "launch_ms_max": max(ms["prefill"])}
+            # the pages' 3 softmax FLOPs per score, kept out of TFLOPS
+            "softmax_gflop_per_launch": 0.75 * info["prefill"]["flops"]
+            / c["d"] / 1e9,
+            **_launch_stats(ms["prefill"])}
         workload.append(f"bf16 causal GQA prefill B={c['B']} Hq={c['Hq']} "
                         f"Hkv={c['Hkv']} N={c['Nq']} d={c['d']}")
     if "decode" in order:
@@ -380,8 +388,7 @@ def main():
                                              ["fa_decode.hip", "fa_device.h"])},
             "algorithmic_bytes": info["decode"]["bytes"],
             "kv_tokens": info["decode"]["kv_tokens"],
-            "launch_ms_mean": t * 1e3,
-            "launch_ms_min": min(ms["decode"])}
+            **_launch_stats(ms["decode"])}
         workload.append(f"paged decode {c['n_req']} requests L~U{{{c['len_min']}.."
                         f"{c['len_max']}}} page {c['page_size']} Hq={c['Hq']} "
                         f"Hkv={c['Hkv']} d={c['d']}")
@@ -393,7 +400,7 @@ def main():
         tf = info["fp8"]["flops"] / t / 1e12
         out["fp8_prefill"] = {
             "value": tf, "unit": "TFLOPS", "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
-            "launch_ms_mean": t * 1e3}
+            **_launch_stats(ms["fp8"])}
         workload.append(f"fp8 e4m3 prefill B={c['B']} H={c['Hq']} N={c['Nq']} "
                         f"d={c['d']}")
         if "value" not in out:
@@ -406,7 +413,7 @@ def main():
             "value": tf, "unit": "TFLOPS", "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
             "algorithmic_gflop_per_launch": info["bwd"]["flops"] / 1e9,
             "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel",
-            "launch_ms_mean": t * 1e3, "launch_ms_min": min(ms["bwd"])}
+            **_launch_stats(ms["bwd"])}
         workload.append(f"bf16 causal GQA backward B={c['B']} Hq={c['Hq']} "
                         f"Hkv={c['Hkv']} N={c['Nq']} d={c['d']}")
         if "value" not in out:
@@ -419,7 +426,7 @@ def main():
             "kernel": "decode_kernel<e4m3 cache> + decode_merge_kernel",
             "algorithmic_bytes": info["decode8"]["bytes"],
             "tokens_per_s": info["decode8"]["kv_tokens"] / t,
-            "launch_ms_mean": t * 1e3, "launch_ms_min": min(ms["decode8"])}
+            **_launch_stats(ms["decode8"])}
         workload.append("paged decode over an e4m3 cache (same requests)")
         if "value" not in out:
             out["value"], out["unit"] = gbs, "GB/s"
@@ -431,14 +438,13 @@ def main():
         tf = info[leg]["flops"] / t / 1e12
         heads = c["B"] * c["Hq"]
         N, d = c["Nq"], c["d"]
-        entry = {"value": tf, "unit": "TFLOPS", "launch_ms_mean": t * 1e3,
-                 "launch_ms_min": min(ms[leg])}
+        entry = {"value": tf, "unit": "TFLOPS", **_launch_stats(ms[leg])}
         if leg == "naive":
             # the pages' traffic ledger, 8Nd + 8N^2 bytes per head
             entry["ledger_bytes"] = heads * (8 * N * d + 8 * N * N)
             entry["ledger_GB/s"] = entry["ledger_bytes"] / t / 1e9
-            entry["kernels"] = ("naive_scores_kernel + naive_softmax_kernel"
-                                " + naive_pv_kernel")
+            entry["kernels"] = ("naive_scores_kernel + "
+                                "naive_softmax_wave_kernel + naive_pv_kernel")
         else:
             entry["ledger_bytes"] = heads * 8 * N * d
         out["bf16_noncausal_" + leg if leg == "naive" else
@@ -450,8 +456,7 @@ def main():
         tf = info["chunked"]["flops"] / t / 1e12
         out["chunked_prefill"] = {
             "value": tf, "unit": "TFLOPS", "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
-            "kernel": "fwd_bf16_kernel<paged>", "launch_ms_mean": t * 1e3,
-            "launch_ms_min": min(ms["chunked"])}
+            "kernel": "fwd_bf16_kernel<paged>", **_launch_stats(ms["chunked"])}
         workload.append("chunked prefill 16 requests x 512 new tokens, paged "
                         "cache U{4096..8192}, Hq=32 Hkv=8 d=128")
         if "value" not in out:
@@ -460,7 +465,7 @@ def main():
         t = statistics.mean(ms["copy"]) / 1e3
         out["copy_calibration"] = {"bytes_per_launch": info["copy"]["bytes"],
                                    "GB/s": info["copy"]["bytes"] / t / 1e9,
-                                   "launch_ms_mean": t * 1e3}
+                                   **_launch_stats(ms["copy"])}
         if "value" not in out:
             out["value"], out["unit"] = info["copy"]["bytes"] / t / 1e9, "GB/s"
     out["config"] = {"workload": " + ".join(workload), "seed": 42,
