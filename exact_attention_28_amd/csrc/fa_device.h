@@ -62,6 +62,12 @@ __device__ __forceinline__ f32x16 mfma_32x32x64_e4m3(i32x8 a, i32x8 b,
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0,
                                                          0, 0);
 }
+// fp4 e2m1 (format code 4, dwords 0-3 of a) x e4m3, no block scaling.
+__device__ __forceinline__ f32x16 mfma_32x32x64_fp4_e4m3(i32x8 a, i32x8 b,
+                                                         f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 0, 0, 0,
+                                                         0, 0);
+}
 
 // ------------------------------------------------------- cross-lane ops
 __device__ __forceinline__ float xor_lane(float x, int mask) {
@@ -97,7 +103,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
 // Four fp32 -> four OCP e4m3 bytes, byte i = x_i (round to nearest even).
 __device__ __forceinline__ uint32_t pack_e4m3x4(float x0, float x1, float x2,
                                                 float x3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  // the first conversion fills the low half and keeps the high half of its
+  // third operand, which the second conversion replaces: x0's bits serve
+  // there, so the register needs no clearing first
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __float_as_int(x0), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
   return (uint32_t)w;
 }

@@ -18,7 +18,8 @@
 // block, and one P V step covers the whole 64-key tile. The V^T operand
 // comes from gfx950's 8-bit LDS transpose read. The sum of the rounded P
 // comes from one more MFMA per tile against an all-ones operand: every
-// output row of ones . P^T is the row sum of P, accumulated exactly.
+// output row of ones . P^T is the row sum of P, accumulated exactly. The
+// ones are given as fp4 (e2m1), which takes four registers instead of eight.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -151,9 +152,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 #pragma unroll
   for (int v = 0; v < 16; ++v) lsum[v] = 0.f;
   RowState st{kNegInf, 0.f, 0.f};
-  // e4m3 1.0 in every byte
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  // e2m1 1.0 (0b0010) in every nibble; an fp4 operand uses dwords 0-3
+  const i32x8 ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222,
+                      0x22222222, 0x22222222, 0x22222222, 0x22222222};
 
   // ---- direct loads. Wave w fills blocks w, w+4, ...; lane l moves chunk
   // l % CPR of the block's slot l / CPR. On the ragged last tile rows past
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         pb[jj] = (int)pack_e4m3x4(p4[0], p4[1], p4[2], p4[3]);
       }
       st.l += sum;
-      lsum = mfma_32x32x64_e4m3(ones, pb, lsum);
+      lsum = mfma_32x32x64_fp4_e4m3(ones, pb, lsum);
       const lds_char* vp = vbuf(cur);
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
