@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int h = lane >> 5;
   const int r32 = lane & 31;
   const int i16 = lane & 15;
@@ -280,32 +280,38 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     __builtin_amdgcn_s_setprio(0);
     // P and dS per element; rows past Nq and causally hidden pairs get 0
     const lds_char* sp = sbuf(cur);
+    // (the test is uniform over the wave: tiles wholly inside the visible
+    // region take the copy of the loop without the per-element test)
     const bool need_mask = (i0 + BR > Nq) || (CAUSAL && i0 + off < wk0 + 31);
     uint32_t pp[2][4], dd[2][4];
+    auto elementwise = [&](auto masked) {
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const f32x4 l2 = *(const lds_f32x4*)(sp + 4 * (8 * gq + 4 * h));
-      const f32x4 dr = *(const lds_f32x4*)(sp + 4 * BR + 4 * (8 * gq + 4 * h));
-      float pv[4], dv4[4];
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 l2 = *(const lds_f32x4*)(sp + 4 * (8 * gq + 4 * h));
+        const f32x4 dr = *(const lds_f32x4*)(sp + 4 * BR + 4 * (8 * gq + 4 * h));
+        float pv[4], dv4[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = 4 * gq + e;
-        float sv = s[v];
-        if (need_mask) {
-          const int i = i0 + 8 * gq + 4 * h + e;
-          const bool vis = (i < Nq) & (!CAUSAL | (key <= i + off));
-          sv = vis ? sv : kNegInf;
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * gq + e;
+          float sv = s[v];
+          if constexpr (decltype(masked)::value) {
+            const int i = i0 + 8 * gq + 4 * h + e;
+            const bool vis = (i < Nq) & (!CAUSAL | (key <= i + off));
+            sv = vis ? sv : kNegInf;
+          }
+          pv[e] = fast_exp2(__builtin_fmaf(sv, c, -l2[e]));
+          dv4[e] = pv[e] * (p[v] - dr[e]);
         }
-        pv[e] = fast_exp2(__builtin_fmaf(sv, c, -l2[e]));
-        dv4[e] = pv[e] * (p[v] - dr[e]);
+        // element pairs of rows 16j + {4h.., 8 + 4h..}: j = gq / 2
+        const int j = gq >> 1, t2 = 2 * (gq & 1);
+        pp[j][t2] = pack_bf16x2(pv[0], pv[1]);
+        pp[j][t2 + 1] = pack_bf16x2(pv[2], pv[3]);
+        dd[j][t2] = pack_bf16x2(dv4[0], dv4[1]);
+        dd[j][t2 + 1] = pack_bf16x2(dv4[2], dv4[3]);
       }
-      // element pairs of rows 16j + {4h.., 8 + 4h..}: j = gq / 2
-      const int j = gq >> 1, t2 = 2 * (gq & 1);
-      pp[j][t2] = pack_bf16x2(pv[0], pv[1]);
-      pp[j][t2 + 1] = pack_bf16x2(pv[2], pv[3]);
-      dd[j][t2] = pack_bf16x2(dv4[0], dv4[1]);
-      dd[j][t2 + 1] = pack_bf16x2(dv4[2], dv4[3]);
-    }
+    };
+    if (need_mask) elementwise(std::true_type{});
+    else elementwise(std::false_type{});
     // dV^T += dO^T P and dK^T += Q^T dS, 16 rows per MFMA
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -373,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int h = lane >> 5;
   const int r32 = lane & 31;
   const int i16 = lane & 15;
@@ -459,28 +465,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         p[kb] = mfma_32x32x16_bf16(lds_row16(vp + rfrag(kb) + T::chunk_off(2 * sd)), of[sd], p[kb]);
       }
     __builtin_amdgcn_s_setprio(0);
+    // (uniform over the wave: tiles wholly inside the visible region take
+    // the copy of the loop without the per-element test)
     const bool need_mask = (n0 + BN > Nk) || (CAUSAL && n0 + BN - 1 > wrow0 + off);
     const int lim = CAUSAL ? min(Nk - 1, row + off) : Nk - 1;
     uint32_t dd[2][2][4];
+    auto elementwise = [&](auto masked) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float ds[16];
+      for (int kb = 0; kb < 2; ++kb) {
+        float ds[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float sv = s[kb][v];
-        if (need_mask) {
-          const int kk = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (kk > lim) sv = kNegInf;
+        for (int v = 0; v < 16; ++v) {
+          float sv = s[kb][v];
+          if constexpr (decltype(masked)::value) {
+            const int kk = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (kk > lim) sv = kNegInf;
+          }
+          const float pv = fast_exp2(__builtin_fmaf(sv, c, -l2));
+          ds[v] = pv * (p[kb][v] - dr);
         }
-        const float pv = fast_exp2(__builtin_fmaf(sv, c, -l2));
-        ds[v] = pv * (p[kb][v] - dr);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2)
+            dd[kb][j][t2] = pack_bf16x2(ds[8 * j + 2 * t2], ds[8 * j + 2 * t2 + 1]);
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2)
-          dd[kb][j][t2] = pack_bf16x2(ds[8 * j + 2 * t2], ds[8 * j + 2 * t2 + 1]);
-    }
+    };
+    if (need_mask) elementwise(std::true_type{});
+    else elementwise(std::false_type{});
     // dQ^T += K^T dS^T, 16 keys per MFMA
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
