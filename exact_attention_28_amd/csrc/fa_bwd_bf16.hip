@@ -217,9 +217,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const int per_head = nqt - t0;
   const int n_it = G * per_head;
 
-  auto issue = [&](int it, auto buf) {
-    const int g = it % G;
-    const int t = nqt - 1 - it / G;
+  // iteration it takes head g = it % G of the group and query tile
+  // t = nqt - 1 - it / G; (g, t) are carried from one iteration to the
+  // next instead of divided out
+  auto issue = [&](int g, int t, auto buf) {
     const long qb = (long)(ti.b * Hq + hk * G + g) * Nq;
     load_tile<D, T>(Q + qb * D, BR * t, Nq, qbuf(buf), w, lane);
     load_tile<D, T>(dO + qb * D, BR * t, Nq, obuf(buf), w, lane);
@@ -245,7 +246,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
   constexpr std::integral_constant<int, 0> B0{};
   constexpr std::integral_constant<int, 1> B1{};
-  if (n_it > 0) issue(0, B0);
+  if (n_it > 0) issue(0, nqt - 1, B0);
+  int cg = 0, ct = nqt - 1;  // (g, t) of the current iteration
 
   auto step = [&](int it, auto par) {
     constexpr int P = decltype(par)::value;
@@ -255,11 +257,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     // last read before the previous barrier
     wait_vm0();
     __syncthreads();
-    if (it + 1 < n_it) issue(it + 1, nxt);
-    const int g = it % G;
-    const int t = nqt - 1 - it / G;
+    int ng = cg + 1, nt = ct;
+    if (ng == G) { ng = 0; --nt; }
+    if (it + 1 < n_it) issue(ng, nt, nxt);
+    const int t = ct;
+    cg = ng;
+    ct = nt;
     const int i0 = BR * t;
-    (void)g;
     if (CAUSAL && i0 + BR - 1 + off < wk0) return;  // no row sees these keys
     const lds_char* qp = qbuf(cur);
     const lds_char* op = obuf(cur);
