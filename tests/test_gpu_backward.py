@@ -75,6 +75,7 @@ def _check(out, ref, what, names=("dQ", "dK", "dV")):
     (1, 2, 2, 300, 96, 128, True),       # Nq > Nk: early rows see no key
     (1, 2, 2, 333, 257, 64, False),
     (3, 6, 2, 150, 200, 128, True),      # odd group size, B = 3
+    (1, 2, 1, 1000, 1100, 128, True),    # many interior and diagonal tiles
 ])
 def test_backward_matches_oracle(fa, B, Hq, Hkv, Nq, Nk, d, causal):
     out, ref = _run(fa, B, Hq, Hkv, Nq, Nk, d, causal, seed=Nq + Nk + d)
