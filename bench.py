@@ -164,8 +164,8 @@ def main():
                     help="comma list of legs to run (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for "
-              f"--gpus {args.gpus}); multi-GPU sharding is not implemented",
+        print(f"bench.py: measures one GPU only (asked for --gpus "
+              f"{args.gpus}); multi-GPU sharding is not implemented",
               file=sys.stderr)
         sys.exit(2)
 
