@@ -121,12 +121,22 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const __bf16* __restrict__ O, const __bf16* __restrict__ dO,
     const float* __restrict__ LSE, float* __restrict__ Dv,
-    float* __restrict__ L2, long rows) {
+    float* __restrict__ L2, long rows, long rows_padded) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
   const long r = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;
   const int cc = threadIdx.x % LPR;
+  // the padding rows after the last head are read by the last query tile
+  // of the dK/dV kernel (for rows that do not exist, so masked): they get
+  // D = 0 and L2 = +inf (P = 0) here, whatever the workspace held before
+  if (r >= rows) {
+    if (r < rows_padded && cc == 0) {
+      Dv[r] = 0.f;
+      L2[r] = __builtin_inff();
+    }
+    return;
+  }
   float acc = 0.f;
-  if (r < rows) {
+  {
     const bf16x8 a = *reinterpret_cast<const bf16x8*>(O + r * D + 8 * cc);
     const bf16x8 b = *reinterpret_cast<const bf16x8*>(dO + r * D + 8 * cc);
 #pragma unroll
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   }
 #pragma unroll
   for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
-  if (r < rows && cc == 0) {
+  if (cc == 0) {
     Dv[r] = acc;
     const float l = LSE[r];
     L2[r] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
@@ -227,7 +237,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     if (w == 0) {
       // the tile's 32 L2 values (lanes 0-31) then its 32 D values, one
       // dword per lane; rows past Nq read the next head's values or the
-      // workspace's padding (never used)
+      // padding the prep kernel fills (masked either way, and finite or
+      // +inf L2 with finite D, so P and dS come out exactly 0)
       const float* src = (lane < 32 ? L2 : Dv) + qb + BR * t + (lane & 31);
       __builtin_amdgcn_global_load_lds(
           src, (__attribute__((address_space(3))) void*)sbuf(buf), 4, 0, 0);
@@ -541,12 +552,14 @@ template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {
   const long rows = (long)a.B * a.Hq * a.Nq;
   float* Dv = static_cast<float*>(a.ws);
-  float* L2 = Dv + bwd_rows_padded(rows);
+  float* L2 = Dv + bwd_rows_padded(rows);  // both arrays rows_padded long
   const float c = a.scale * kLog2e;
-  const long prep_blocks = (rows * (D / 8) + 255) / 256;
+  const long rows_padded = bwd_rows_padded(rows);
+  const long prep_blocks = (rows_padded * (D / 8) + 255) / 256;
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)prep_blocks),
                      dim3(256), 0, a.stream, static_cast<const __bf16*>(a.o),
-                     static_cast<const __bf16*>(a.dout), a.lse, Dv, L2, rows);
+                     static_cast<const __bf16*>(a.dout), a.lse, Dv, L2, rows,
+                     rows_padded);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long kv_blocks = (long)((a.Nk + 127) / 128) * a.Hkv * a.B;

@@ -159,3 +159,28 @@ def test_backward_full_workload_sampled(fa):
             _check([dk[:, :, r0:], dv[:, :, r0:]],
                    [ref[1][:, :, r0:], ref[2][:, :, r0:]],
                    "full workload dK, dV of the last keys", names=("dK", "dV"))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_workspace_contents_do_not_matter(fa, d):
+    # Nq not a multiple of the 32-row tile: the last query tile of the last
+    # head reads the workspace rows after the real ones. The workspace is
+    # filled with NaN bytes first; the gradients must not see them.
+    B, Hq, Hkv, N, causal = 1, 2, 1, 200, True
+    inp = W.prefill_inputs(B, Hq, Hkv, N, N, d, dtype="bf16", causal=causal,
+                           seed=77 + d)
+    g = W.upstream_grad((B, Hq, N, d), seed=78 + d)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (inp.q, inp.k, inp.v, g))
+    print(f"bwd NaN-filled workspace d={d}", flush=True)
+    o, lse = fa.attention(q, k, v, causal=causal, scale=inp.scale)
+    need = fa.fa_bwd_workspace_size(B, Hq, N)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, causal=causal,
+                                       scale=inp.scale, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(W.as_f64(inp.q), W.as_f64(inp.k),
+                                    W.as_f64(inp.v), W.as_f64(g), inp.scale,
+                                    causal=causal)
+    out = [t.double().cpu().numpy() for t in (dq, dk, dv)]
+    _check(out, ref, f"bwd NaN-filled workspace d={d}")
