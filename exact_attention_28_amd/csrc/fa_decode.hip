@@ -296,7 +296,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
       pr[v] = fast_exp2(__builtin_fmaf(acc[v], a.c, -mref));
       lp += pr[v];
     }
-    // O[g, d] += sum over this lane's 4 tokens of P[token, g] * V[token, d]
+    // O[g, d] += sum over this lane's 4 tokens of P[token, g] * V[token, d].
+    // A token past the piece (the tail of a request's last page) has P = 0,
+    // but its V row is a cache slot whose contents are unspecified: it is
+    // taken as 0, so that 0 * NaN cannot reach O.
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       float vf[DL];
@@ -309,6 +312,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
       } else {
 #pragma unroll
         for (int e = 0; e < DL / 4; ++e) e4m3x4_to_f32(pr_in.v[rr][e], vf + 4 * e);
+      }
+      if (tok0 + rr >= lim) {
+#pragma unroll
+        for (int e = 0; e < DL; ++e) vf[e] = 0.f;
       }
       PvAccumulate<GP, GP, DL>::run(o, pr[rr], vf);
     }

@@ -11,6 +11,7 @@ Reduced sizes span several tiles and ragged tails; the full workloads are
 checked on sampled rows (each output row depends only on its own query, so
 the oracle evaluates exactly those rows).
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -478,3 +479,56 @@ def test_paged_prefill_long_context_sampled(fa):
     # alignment is the same
     _compare(o[:, :, -16:], lse[:, :, -16:], ro, rl, "bf16",
              "paged prefill long, last 16 rows")
+
+
+# ------------------------------------------- unspecified cache slot contents
+# Slots of a request's last page at or past its length are outside the
+# request: whatever they hold must not reach the output. The pools' tail
+# slots are set to NaN here (finite poison elsewhere in this file cannot
+# show a 0 * NaN), for both decodes and the chunked prefill.
+def _nan_tails(di):
+    kp, vp = di.k_pool.clone(), di.v_pool.clone()
+    bt, sl = di.block_table.numpy(), di.seq_lens.numpy()
+    page = di.page_size
+    for r, L in enumerate(sl):
+        L = int(L)
+        if L % page == 0:
+            continue
+        phys = int(bt[r, L // page])
+        kp[phys, L % page:] = float("nan")
+        vp[phys, L % page:] = float("nan")
+    return dataclasses.replace(di, k_pool=kp, v_pool=vp)
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_decode_nan_in_unused_slots(fa, num_splits):
+    lens = [1, 15, 17, 33, 100, 255, 257, 1000]
+    di = _nan_tails(W.decode_inputs(len(lens), 8, 2, 128, lens=lens,
+                                    max_pages=80, seed=11))
+    print(f"decode NaN tails splits={num_splits}", flush=True)
+    o, lse = _gpu_decode(fa, di, num_splits)
+    ro, rl = _oracle_decode(di)
+    _compare(o, lse, ro, rl, "bf16", f"decode NaN tails splits={num_splits}")
+
+
+def test_decode_fp8_cache_nan_in_unused_slots(fa):
+    lens = [1, 15, 17, 33, 100, 255, 257, 1000]
+    di = _nan_tails(W.decode_inputs(len(lens), 8, 2, 128, lens=lens,
+                                    max_pages=80, seed=12, kv_dtype="fp8"))
+    print("fp8-cache decode NaN tails", flush=True)
+    o, lse = _gpu_decode_fp8(fa, di)
+    ro, rl = _oracle_decode_fp8(di)
+    _compare(o, lse, ro, rl, "bf16", "fp8-cache decode NaN tails")
+
+
+def test_paged_prefill_nan_in_unused_slots(fa):
+    lens = [5, 17, 300, 777]
+    di = _nan_tails(W.paged_prefill_inputs(len(lens), 8, 2, 128, 17,
+                                           lens=lens, max_pages=70, seed=13))
+    print("paged prefill NaN tails", flush=True)
+    o, lse = _gpu_paged_prefill(fa, di, True)
+    ro, rl = oracle.paged_prefill(W.as_f64(di.q), W.as_f64(di.k_pool),
+                                  W.as_f64(di.v_pool), di.block_table.numpy(),
+                                  di.seq_lens.numpy(), di.page_size, di.scale,
+                                  causal=True)
+    _compare(o, lse, ro, rl, "bf16", "paged prefill NaN tails")
