@@ -532,3 +532,63 @@ def test_paged_prefill_nan_in_unused_slots(fa):
                                   di.seq_lens.numpy(), di.page_size, di.scale,
                                   causal=True)
     _compare(o, lse, ro, rl, "bf16", "paged prefill NaN tails")
+
+
+# ------------------------------------------------------ LSE not wanted
+# The decodes and the chunked prefill take lse = NULL; O must be the same as
+# with an LSE buffer (whole requests written directly and split requests
+# merged both skip the LSE store).
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_decode_without_lse(fa, num_splits):
+    lens = [0, 1, 17, 300, 1000, 2049]
+    di = W.decode_inputs(len(lens), 8, 2, 128, lens=lens, max_pages=140,
+                         seed=21)
+    dev = torch.device("cuda:0")
+    q, kp, vp = di.q.to(dev), di.k_pool.to(dev), di.v_pool.to(dev)
+    bt, sl = di.block_table.to(dev), di.seq_lens.to(dev)
+    B, Hq, d = q.shape
+    npg, page, Hkv, _ = kp.shape
+    maxp = bt.shape[1]
+    print(f"decode lse=NULL splits={num_splits}", flush=True)
+    need = fa.fa_paged_decode_workspace_size(B, Hq, Hkv, d, maxp, page,
+                                             num_splits)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=dev)
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16,
+                     device=dev)
+    fa.fa_paged_decode(q, kp, vp, bt, sl, page, npg, B, Hq, Hkv, d, maxp,
+                       di.scale, out, None, ws, ws.numel(), num_splits)
+    torch.cuda.synchronize()
+    ref_o, _ = _gpu_decode(fa, di, num_splits)
+    assert np.array_equal(out.double().cpu().numpy(), ref_o)
+    if num_splits == 0:
+        d8 = W.decode_inputs(len(lens), 8, 2, 128, lens=lens, max_pages=140,
+                             seed=22, kv_dtype="fp8")
+        k8, v8 = d8.k_pool.to(dev), d8.v_pool.to(dev)
+        q8, bt8, sl8 = d8.q.to(dev), d8.block_table.to(dev), d8.seq_lens.to(dev)
+        out8 = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16,
+                          device=dev)
+        fa.fa_paged_decode_fp8kv(q8, k8, v8, bt8, sl8, page, k8.shape[0], B,
+                                 Hq, Hkv, d, maxp, d8.scale, d8.kv_descale,
+                                 out8, None, ws, ws.numel(), 0)
+        torch.cuda.synchronize()
+        ref8, _ = _gpu_decode_fp8(fa, d8)
+        assert np.array_equal(out8.double().cpu().numpy(), ref8)
+
+
+def test_paged_prefill_without_lse(fa):
+    lens = [5, 300, 777]
+    di = W.paged_prefill_inputs(len(lens), 8, 2, 128, 40, lens=lens,
+                                max_pages=70, seed=23)
+    dev = torch.device("cuda:0")
+    q, kp, vp = di.q.to(dev), di.k_pool.to(dev), di.v_pool.to(dev)
+    bt, sl = di.block_table.to(dev), di.seq_lens.to(dev)
+    B, Hq, Nq, d = q.shape
+    npg, page, Hkv, _ = kp.shape
+    print("paged prefill lse=NULL", flush=True)
+    out = torch.full((B, Hq, Nq, d), float("nan"), dtype=torch.bfloat16,
+                     device=dev)
+    fa.fa_paged_prefill(q, kp, vp, bt, sl, page, npg, B, Hq, Hkv, Nq, d,
+                        bt.shape[1], di.scale, True, out, None)
+    torch.cuda.synchronize()
+    ref_o, _ = _gpu_paged_prefill(fa, di, True)
+    assert np.array_equal(out.double().cpu().numpy(), ref_o)
