@@ -592,3 +592,35 @@ def test_paged_prefill_without_lse(fa):
     torch.cuda.synchronize()
     ref_o, _ = _gpu_paged_prefill(fa, di, True)
     assert np.array_equal(out.double().cpu().numpy(), ref_o)
+
+
+# ------------------------------------------------------ many requests
+def test_decode_many_requests(fa):
+    # 600 requests of 0..300 tokens: many pieces per range, bookkeeping for
+    # a batch well past one workgroup's worth of requests
+    rng = np.random.default_rng(31)
+    lens = rng.integers(0, 301, size=600).tolist()
+    di = W.decode_inputs(len(lens), 8, 2, 128, lens=lens, max_pages=20,
+                         seed=31)
+    ro, rl = _oracle_decode(di)
+    for ns in (0, 7):
+        print(f"decode 600 requests splits={ns}", flush=True)
+        o, lse = _gpu_decode(fa, di, ns)
+        _compare(o, lse, ro, rl, "bf16", f"decode 600 requests splits={ns}")
+
+
+@pytest.mark.parametrize("n_req", [256, 257])
+def test_paged_prefill_many_requests(fa, n_req):
+    # 256 requests are ordered longest first inside the kernel; from 257 on
+    # the batch runs in index order: both must give the oracle's result
+    rng = np.random.default_rng(n_req)
+    lens = rng.integers(4, 200, size=n_req).tolist()
+    di = W.paged_prefill_inputs(n_req, 4, 2, 64, 4, lens=lens, max_pages=13,
+                                seed=n_req)
+    print(f"paged prefill {n_req} requests", flush=True)
+    o, lse = _gpu_paged_prefill(fa, di, True)
+    ro, rl = oracle.paged_prefill(W.as_f64(di.q), W.as_f64(di.k_pool),
+                                  W.as_f64(di.v_pool), di.block_table.numpy(),
+                                  di.seq_lens.numpy(), di.page_size, di.scale,
+                                  causal=True)
+    _compare(o, lse, ro, rl, "bf16", f"paged prefill {n_req} requests")
