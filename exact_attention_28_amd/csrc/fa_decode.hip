@@ -322,8 +322,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   };
 
   // Pieces: the part of request b inside this range, pages [p, pe).
-  // pages in flight per wave: an e4m3 page is half the bytes, so it keeps
-  // more of them in flight for the same bytes
+  // pages in flight per wave: two for both storages (an e4m3 page is half
+  // the bytes, but three or four of them in flight measured slower)
   constexpr int NS = KV8 ? kSlots8 : 2;
   Regs slot_regs[NS];
   bool slot_bad[NS];
