@@ -10,8 +10,9 @@
 // with dK, dV of a KV head summed over the query heads of its group.
 //
 // Three kernels, no atomics (the result does not depend on scheduling):
-//  * bwd_prep_kernel: D_i and LSE_i * log2(e) (+inf for a row that saw no
-//    key, so its P evaluates to 0) into the workspace.
+//  * bwd_prep_kernel: -D_i and LSE_i * log2(e) (+inf for a row that saw no
+//    key, so its P evaluates to 0) into the workspace; -D_i is the starting
+//    value of the dP products, which then leave dP - D directly.
 //  * bwd_dkdv_kernel (key-outer): a workgroup owns 128 keys of one (batch,
 //    KV head), 32 per wave, with the wave's K and V rows held as MFMA
 //    operands in registers; it streams 32-row tiles of Q and dO (and their
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 #pragma unroll
   for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
   if (cc == 0) {
-    Dv[r] = acc;
+    Dv[r] = -acc;  // stored negated: the dP products start from it
     const float l = LSE[r];
     L2[r] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
   }
@@ -282,9 +283,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     // The MFMA phases run at raised issue priority, so while one wave
     // feeds the matrix cores the other wave of the SIMD fills in with its
     // VALU work.
+    // S starts at 0; dP starts at -D of its row (element v: row 8(v/4) +
+    // 4h + v%4), so the products leave dP - D and dS = P (dP - D) needs no
+    // subtraction
+    const lds_char* sp = sbuf(cur);
     f32x16 s, p;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = p[v] = 0.f;
+    for (int gq = 0; gq < 4; ++gq) {
+      const f32x4 nd = *(const lds_f32x4*)(sp + 4 * BR + 4 * (8 * gq + 4 * h));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[4 * gq + e] = 0.f;
+        p[4 * gq + e] = nd[e];
+      }
+    }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int sd = 0; sd < D / 16; ++sd) {
@@ -294,7 +306,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     }
     __builtin_amdgcn_s_setprio(0);
     // P and dS per element; rows past Nq and causally hidden pairs get 0
-    const lds_char* sp = sbuf(cur);
     // (the test is uniform over the wave: tiles wholly inside the visible
     // region take the copy of the loop without the per-element test)
     const bool need_mask = (i0 + BR > Nq) || (CAUSAL && i0 + off < wk0 + 31);
@@ -303,7 +314,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const f32x4 l2 = *(const lds_f32x4*)(sp + 4 * (8 * gq + 4 * h));
-        const f32x4 dr = *(const lds_f32x4*)(sp + 4 * BR + 4 * (8 * gq + 4 * h));
         float pv[4], dv4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
             sv = vis ? sv : kNegInf;
           }
           pv[e] = fast_exp2(__builtin_fmaf(sv, c, -l2[e]));
-          dv4[e] = pv[e] * (p[v] - dr[e]);
+          dv4[e] = pv[e] * p[v];
         }
         // element pairs of rows 16j + {4h.., 8 + 4h..}: j = gq / 2
         const int j = gq >> 1, t2 = 2 * (gq & 1);
@@ -422,7 +432,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     of[s] = *reinterpret_cast<const bf16x8*>(dO + (qbase + rowc) * D + 16 * s + 8 * h);
   }
   const float l2 = L2[qbase + rowc];
-  const float dr = Dv[qbase + rowc];
+  // -D of this lane's row in every element: the accumulator input of the
+  // first dP product of each tile, so the products leave dP - D
+  f32x16 negd;
+  {
+    const float nd = Dv[qbase + rowc];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) negd[v] = nd;
+  }
   f32x16 acc[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
@@ -466,18 +483,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const lds_char* kp = kbuf(cur);
     const lds_char* vp = vbuf(cur);
     // S^T = K Q^T, dP^T = V dO^T: lane = row r32, keys 32kb + 8(v/4) + 4h + v%4
+    // (dP^T starts from -D of the lane's row: the first product takes negd
+    // as its accumulator input)
     f32x16 s[2], p[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = p[kb][v] = 0.f;
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int sd = 0; sd < D / 16; ++sd)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = mfma_32x32x16_bf16(lds_row16(kp + rfrag(kb) + T::chunk_off(2 * sd)), qf[sd], s[kb]);
-        p[kb] = mfma_32x32x16_bf16(lds_row16(vp + rfrag(kb) + T::chunk_off(2 * sd)), of[sd], p[kb]);
+        p[kb] = mfma_32x32x16_bf16(lds_row16(vp + rfrag(kb) + T::chunk_off(2 * sd)), of[sd],
+                                   sd == 0 ? negd : p[kb]);
       }
     __builtin_amdgcn_s_setprio(0);
     // (uniform over the wave: tiles wholly inside the visible region take
@@ -497,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             if (kk > lim) sv = kNegInf;
           }
           const float pv = fast_exp2(__builtin_fmaf(sv, c, -l2));
-          ds[v] = pv * (p[kb][v] - dr);
+          ds[v] = pv * p[kb][v];
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
