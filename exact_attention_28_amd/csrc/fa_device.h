@@ -255,15 +255,35 @@ __device__ __forceinline__ void online_softmax_tile(f32x16 (&s)[NKB],
 // move). softmax_exp_pack: P = exp2(s*c - m_ref) summed into l, rounded to
 // bf16 and packed in the PV operand order (block kb, 16-key step j, pairs),
 // the rounded values summed into lr.
+// softmax_reference in two parts, so that a caller can take the row max of
+// a tile early (tile_max) and move the reference later (move_reference).
 template <int NKB>
-__device__ __forceinline__ float softmax_reference(f32x16 (&s)[NKB],
-                                                   RowState& st, float c) {
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[NKB]) {
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-  mx = max_halves(mx);
+  return max_halves(mx);
+}
+__device__ __forceinline__ float move_reference(float mx, RowState& st,
+                                                float c) {
+  const float mxs = mx * c;
+  float alpha = 1.f;
+  if (__any(mxs > st.m + kTau)) {
+    const float mnew = fmaxf(st.m, mxs);
+    alpha = (st.m == kNegInf) ? 0.f : fast_exp2(st.m - mnew);
+    st.l *= alpha;
+    st.lr *= alpha;
+    st.m = mnew;
+  }
+  return alpha;
+}
+
+template <int NKB>
+__device__ __forceinline__ float softmax_reference(f32x16 (&s)[NKB],
+                                                   RowState& st, float c) {
+  const float mx = tile_max<NKB>(s);
   const float mxs = mx * c;
   float alpha = 1.f;
   if (__any(mxs > st.m + kTau)) {

@@ -288,7 +288,14 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 sc[2];
-  if (nt > 0 && !skip_tile(0)) qk(B0, sc);
+  // row max of the next tile's scores, taken where S is formed (beside the
+  // P.V products of the previous tile); a tile that needs masking takes its
+  // max again after the mask
+  float mx_next = kNegInf;
+  if (nt > 0 && !skip_tile(0)) {
+    qk(B0, sc);
+    mx_next = tile_max<2>(sc);
+  }
   __syncthreads();  // K buffer 0 is refilled below
 
   // One key tile: S(t) arrives in sc; S(t+1) is computed into sn while P(t)
@@ -314,6 +321,7 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
       // mask the ragged end of the key range and the causal diagonal
       const bool need_mask =
           (n0 + kBN > nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
+      float mx = mx_next;
       if (need_mask) {
         const int lim = CAUSAL ? min(nk - 1, row + off) : nk - 1;
 #pragma unroll
@@ -323,8 +331,9 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
             const int key = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
             if (key > lim) sc[kb][v] = kNegInf;
           }
+        mx = tile_max<2>(sc);
       }
-      const float alpha = softmax_reference<2>(sc, st, c);
+      const float alpha = move_reference(mx, st, c);
       // rescale O before the MFMA work below, so that the S(t+1) product
       // and the P(t) arithmetic share one branch-free block
       if (__any(alpha != 1.f)) {
@@ -366,6 +375,7 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
             o[mb] = mfma_32x32x16_bf16(a, pb, o[mb]);
           }
         }
+      mx_next = tile_max<2>(sn);
       __builtin_amdgcn_s_setprio(0);
     }
     // tile t+1 needs K(t+2) and V(t+1), so only the V(t+2) loads just
