@@ -248,15 +248,13 @@ __device__ __forceinline__ void online_softmax_tile(f32x16 (&s)[NKB],
   st.l += sum;
 }
 
-// The same update split in two, so that a caller can put independent MFMA
-// work between them. softmax_reference: row max of the tile (masked
-// entries -inf), lazy move of the exponent reference, l and lr rescaled;
-// returns the factor O must be multiplied by (1 when the reference did not
-// move). softmax_exp_pack: P = exp2(s*c - m_ref) summed into l, rounded to
-// bf16 and packed in the PV operand order (block kb, 16-key step j, pairs),
-// the rounded values summed into lr.
-// softmax_reference in two parts, so that a caller can take the row max of
-// a tile early (tile_max) and move the reference later (move_reference).
+// The same update split in parts, so that a caller can put independent MFMA
+// work between them. tile_max: row max of a tile (masked entries -inf);
+// move_reference: lazy move of the exponent reference for that max, l and
+// lr rescaled, returning the factor O must be multiplied by (1 when the
+// reference did not move). softmax_exp_pack: P = exp2(s*c - m_ref) summed
+// into l, rounded to bf16 and packed in the PV operand order (block kb,
+// 16-key step j, pairs), the rounded values summed into lr.
 template <int NKB>
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[NKB]) {
   float mx = kNegInf;
@@ -268,23 +266,7 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[NKB]) {
 }
 __device__ __forceinline__ float move_reference(float mx, RowState& st,
                                                 float c) {
-  const float mxs = mx * c;
-  float alpha = 1.f;
-  if (__any(mxs > st.m + kTau)) {
-    const float mnew = fmaxf(st.m, mxs);
-    alpha = (st.m == kNegInf) ? 0.f : fast_exp2(st.m - mnew);
-    st.l *= alpha;
-    st.lr *= alpha;
-    st.m = mnew;
-  }
-  return alpha;
-}
-
-template <int NKB>
-__device__ __forceinline__ float softmax_reference(f32x16 (&s)[NKB],
-                                                   RowState& st, float c) {
-  const float mx = tile_max<NKB>(s);
-  const float mxs = mx * c;
+  const float mxs = mx * c;  // c > 0, so max commutes with the scaling
   float alpha = 1.f;
   if (__any(mxs > st.m + kTau)) {
     const float mnew = fmaxf(st.m, mxs);

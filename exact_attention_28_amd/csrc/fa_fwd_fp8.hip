@@ -241,7 +241,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   wait_vm0();
   __syncthreads();
   f32x16 sc[2];
-  if (nt > 0 && !skip_tile(0)) qk(B0, sc);
+  // row max of the next tile's scores, taken beside the previous tile's P.V
+  // products; a tile that needs masking takes its max again after the mask
+  float mx_next = kNegInf;
+  if (nt > 0 && !skip_tile(0)) {
+    qk(B0, sc);
+    mx_next = tile_max<2>(sc);
+  }
   __syncthreads();  // K buffer 0 is refilled below
 
   // One key tile t (parity P): S(t) arrives in sc, S(t+1) is computed into
@@ -258,6 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     if (!skip_tile(t)) {
       const bool need_mask =
           (n0 + kBN > Nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
+      float mx = mx_next;
       if (need_mask) {
         const int lim = CAUSAL ? min(Nk - 1, row + off) : Nk - 1;
 #pragma unroll
@@ -267,8 +274,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
             const int key = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
             if (key > lim) sc[kb][v] = kNegInf;
           }
+        mx = tile_max<2>(sc);
       }
-      const float alpha = softmax_reference<2>(sc, st, c);
+      const float alpha = move_reference(mx, st, c);
       if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
@@ -313,6 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         }
         o[mb] = mfma_32x32x64_e4m3(a, pb, o[mb]);
       }
+      mx_next = tile_max<2>(sn);
       __builtin_amdgcn_s_setprio(0);
     }
     wait_vm0();
