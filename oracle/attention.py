@@ -34,8 +34,8 @@ notes of the repository):
   j <= i + (Nk - Nq). For Nq == Nk this is the lower triangle of
   [Capstone §7.3, question 2]; for a single decode query it sees all keys.
 * Grouped-query attention: query head h reads KV head h // (Hq // Hkv).
-* A row whose keys are all masked has l = 0: its O is 0 and its LSE is -inf
-  (never NaN). The guard mirrors the alpha = 0 case of [Capstone lab 2].
+* A row whose keys are all masked has l = 0 (an empty sum): its O is 0 and
+  its LSE is -inf (never NaN).
 * FP8: values are e4m3 codes times a per-tensor fp32 scale; the oracle
   multiplies them out in fp64 (exact) and does NOT model the kernel's
   re-quantisation of P ([FA3-guide] ``flash_attn_v3_fp8`` listing).
@@ -101,24 +101,26 @@ def safe_softmax(x):
 def online_softmax_stats(blocks):
     """Streaming (m, l) over a sequence of blocks [Capstone §2.2 steps 3-4].
 
-    For each block B: m_new = max(m, max B); l = l * exp(m - m_new) +
-    sum exp(B - m_new). The decay factor is taken as 0 while m is still -inf
-    (the guard of [Capstone lab 2]). Returns the list of (m, l) after each
-    block, so a test can compare every intermediate state with the page's
-    worked example.
+    Each block's own statistics (m_B, l_B) come from the three-pass
+    ``softmax_stats``; they are folded into the running pair with the
+    two-block merge of step 4: m = max(m_run, m_B) and
+    l = l_run * exp(m_run - m) + l_B * exp(m_B - m). A side that has seen no
+    finite value (m = -inf, l = 0) adds nothing to the sum. Returns the list
+    of (m, l) after each block, so a test can compare every intermediate
+    state with the page's worked example.
     """
-    m, l = -math.inf, 0.0
+    def weight(mx, m):
+        return 0.0 if mx == -math.inf else math.exp(mx - m)
+
+    m_run, l_run = -math.inf, 0.0
     states = []
     for blk in blocks:
-        blk = np.asarray(blk, dtype=np.float64)
-        m_new = max(m, float(np.max(blk)))
-        if m_new == -math.inf:
-            states.append((m, l))
-            continue
-        alpha = 0.0 if m == -math.inf else math.exp(m - m_new)
-        l = l * alpha + float(np.sum(np.exp(blk - m_new)))
-        m = m_new
-        states.append((m, l))
+        m_b, l_b = softmax_stats(blk)
+        m = max(m_run, m_b)
+        if m > -math.inf:
+            l_run = l_run * weight(m_run, m) + l_b * weight(m_b, m)
+            m_run = m
+        states.append((m_run, l_run))
     return states
 
 

@@ -57,34 +57,33 @@ def test_worked_example_three_pass_equals_stream():
 
 
 def test_lab2_vector_stream_vs_three_pass():
-    """An independent block-streaming softmax reaches the oracle's P."""
+    """Block-wise softmax with one log-sum-exp combine over the blocks (the
+    merge of [Capstone §2.2 step 4] applied to every block at once) reaches
+    the oracle's P, for the lab's vector and block size."""
     g = _load("online_softmax_lab_vector.json")
     x, bs = g["vector"], g["block_size"]
-    # streaming written here from the page's recurrence, pure Python
-    m, l, recs = -math.inf, 0.0, []
-    for i in range(0, len(x), bs):
-        blk = x[i:i + bs]
-        mn = max(m, max(blk))
-        a = 0.0 if m == -math.inf else math.exp(m - mn)
-        e = [math.exp(t - mn) for t in blk]
-        l = l * a + sum(e)
-        m = mn
-        recs.append((mn, e))
-    streamed = [ei * math.exp(mb - m) / l for mb, e in recs for ei in e]
+    blocks = [x[i:i + bs] for i in range(0, len(x), bs)]
+    # each block alone: its maximum and its exponentials against it
+    loc = [(max(b), [math.exp(t - max(b)) for t in b]) for b in blocks]
+    M = max(mb for mb, _ in loc)
+    Z = sum(sum(e) * math.exp(mb - M) for mb, e in loc)
+    combined = [ei * math.exp(mb - M) / Z for mb, e in loc for ei in e]
     p = oracle.safe_softmax(x)
-    assert np.max(np.abs(p - np.array(streamed))) <= g["max_abs_diff"] * 4
+    assert np.max(np.abs(p - np.array(combined))) <= g["max_abs_diff"] * 4
     assert abs(p.sum() - 1.0) < 1e-15
     # online_softmax_stats ends in the same (m, l)
-    sm, sl = oracle.online_softmax_stats(
-        [x[i:i + bs] for i in range(0, len(x), bs)])[-1]
-    assert sm == max(x)
-    assert abs(sl - l) < 1e-14
+    sm, sl = oracle.online_softmax_stats(blocks)[-1]
+    assert sm == M
+    assert abs(sl - Z) < 1e-14
 
 
 def test_lab3_tiled_fa2_protocol():
-    """Q-outer / KV-inner tiled FA2 with deferred 1/l (written here from the
-    algorithm of the capstone page §4.1-4.2) vs the oracle, the lab's seed
-    and sizes, error below the lab's bar."""
+    """Tiled attention in block log-sum-exp form vs the oracle, at the lab's
+    seed, sizes and error bar. For each query tile and key block: the
+    block's row maxima m_j, sums l_j and unnormalised product O_j =
+    exp(S_j - m_j) V_j; then all blocks of the tile are combined at once
+    with the merge identity of [Capstone §2.2 step 4] and appendix A Q1
+    (weights exp(m_j - M)), dividing by l only at the end as in §4.2."""
     g = _load("tiled_fa2_lab_protocol.json")
     np.random.seed(g["legacy_numpy_seed"])
     N, d = g["seq_len"], g["head_dim"]
@@ -96,18 +95,18 @@ def test_lab3_tiled_fa2_protocol():
     out = np.zeros_like(Q)
     for i0 in range(0, N, Br):
         Qi = Q[i0:i0 + Br]
-        m = np.full(len(Qi), -np.inf)
-        l = np.zeros(len(Qi))
-        acc = np.zeros((len(Qi), d))
+        ms, ls, os_ = [], [], []
         for j0 in range(0, N, Bc):
-            s = (Qi @ K[j0:j0 + Bc].T) * scale
-            mn = np.maximum(m, s.max(axis=1))
-            p = np.exp(s - mn[:, None])
-            a = np.exp(m - mn)
-            l = l * a + p.sum(axis=1)
-            acc = acc * a[:, None] + p @ V[j0:j0 + Bc]
-            m = mn
-        out[i0:i0 + Br] = acc / l[:, None]
+            s = scale * (Qi @ K[j0:j0 + Bc].T)
+            mj = s.max(axis=1)
+            e = np.exp(s - mj[:, None])
+            ms.append(mj)
+            ls.append(e.sum(axis=1))
+            os_.append(e @ V[j0:j0 + Bc])
+        ms, ls, os_ = np.stack(ms), np.stack(ls), np.stack(os_)
+        w = np.exp(ms - ms.max(axis=0)[None])          # [blocks, rows]
+        out[i0:i0 + Br] = ((w[..., None] * os_).sum(axis=0)
+                           / (w * ls).sum(axis=0)[:, None])
     o, lse = oracle.attention(Q[None, None], K[None, None], V[None, None],
                               scale)
     assert np.max(np.abs(o[0, 0] - out)) < g["pass_if_max_abs_error_below"]
