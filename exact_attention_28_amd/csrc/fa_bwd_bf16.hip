@@ -39,17 +39,10 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = kThreads / 64;
 
-typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
-__device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
-                                   16, 0, 0);
-}
-// s_waitcnt vmcnt(0): the direct loads of this wave have reached LDS.
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // A row-major tile of ROWS rows x D bf16 in LDS, as 1 KB blocks (one direct
 // load instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B. RowTile

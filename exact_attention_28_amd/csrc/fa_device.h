@@ -43,6 +43,19 @@ __device__ __forceinline__ float fast_log2(float x) {
   return __builtin_amdgcn_logf(x);
 }
 
+// ------------------------------------------------ direct global -> LDS
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One 16-byte piece per lane straight from global memory into LDS
+// (global_load_lds_dwordx4): the 64 lanes of the instruction fill 1 KB of
+// contiguous LDS starting at the wave's address l, with no VGPR staging.
+__device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
+                                   16, 0, 0);
+}
+// s_waitcnt vmcnt(0): the direct loads of this wave have reached LDS.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------- MFMA
 __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b,
                                                      f32x16 c) {

@@ -57,15 +57,6 @@ struct Lay {
   static constexpr int BPW = NB / kWaves;       // blocks each wave loads
 };
 
-typedef __attribute__((address_space(3))) char lds_char;
-
-__device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
-                                   16, 0, 0);
-}
-// s_waitcnt vmcnt(0): the direct loads of this wave have reached LDS.
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 // Where K and V come from. Contiguous: [B, Hkv, Nk, d]. Paged (the
 // chunked prefill of [FA3-paged §3.2]): the cache of request b is
 // seq_lens[b] tokens in 16-token pages of a [num_pages, 16, Hkv, d] pool,
@@ -348,7 +339,8 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
       // past the last tile, or beyond this wave's causal rows, the result is
       // never read, and the K buffer it reads is not being written.
       // raised issue priority while this wave feeds the matrix cores: the
-      // other wave of the SIMD (another workgroup) fills in with its VALU work
+      // other wave on the SIMD (a wave of this workgroup: the 83 KB of LDS
+      // leave room for one workgroup per CU) fills in with its VALU work
       __builtin_amdgcn_s_setprio(1);
       qk(nxt, sn);
       softmax_exp_pack<2>(sc, st, c, pw);

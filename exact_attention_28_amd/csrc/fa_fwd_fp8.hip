@@ -81,13 +81,6 @@ __device__ __forceinline__ int v_row(int b, int s) {
   else return 8 * (s & 7) + 4 * (s >> 3) + b;
 }
 
-typedef __attribute__((address_space(3))) char lds_char;
-
-__device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
-                                   16, 0, 0);
-}
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(

@@ -26,16 +26,11 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
-                                   16, 0, 0);
-}
 
 // 64-row tile of D bf16 in LDS, 1 KB blocks at a 1040 B pitch, row r in
 // block r % NB, slot r / NB (16-byte row reads conflict free).
