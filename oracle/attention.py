@@ -64,6 +64,8 @@ __all__ = [
     "safe_softmax",
     "attention",
     "attention_fp8",
+    "round_e4m3",
+    "attention_fp8_p_e4m3",
     "merge_partials",
     "gather_paged_kv",
     "paged_decode",
@@ -201,6 +203,63 @@ def attention_fp8(qc, kc, vc, s_q, s_k, s_v, scale, causal=False, rows=None):
     kx = np.asarray(kc, dtype=np.float64) * float(s_k)
     vx = np.asarray(vc, dtype=np.float64) * float(s_v)
     return attention(qx, kx, vx, scale, causal=causal, rows=rows)
+
+
+def round_e4m3(x):
+    """Round fp64 values to the nearest OCP e4m3fn value, ties to even
+    (the fp8 format of the [FA3-guide] fp8 listing): 3 mantissa bits,
+    exponent bias 7, normal exponents -6..8, subnormal step 2^-9, largest
+    finite value 448 (magnitudes beyond saturate to +-448, as a
+    saturating conversion does). Used only by the report-only diagnostic
+    below; the oracle proper never rounds to e4m3."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)                       # below 2^-6: subnormal step
+    step = np.exp2(e - 3)
+    r = np.round(a / step) * step               # np.round: half to even
+    r = np.minimum(r, 448.0)
+    return np.where(a > 0, np.copysign(r, x), x)
+
+
+def attention_fp8_p_e4m3(qc, kc, vc, s_q, s_k, s_v, scale, causal=False,
+                         rows=None):
+    """REPORT-ONLY diagnostic, never a parity gate: ``attention_fp8`` with
+    the probabilities rounded to e4m3 before the product with V, as the
+    [FA3-guide] fp8 listing casts P to fp8 before its P.V GEMM.
+
+    P is taken relative to the row's global maximum (exp(S - m) in [0, 1],
+    the three-pass form of [Capstone §2.1]), rounded with ``round_e4m3``,
+    and O = round(P) V / sum(round(P)): the rounded weights divided by
+    their own sum. LSE is that of ``attention_fp8`` (unrounded). The
+    kernel's own rounding is of P against a running reference, so this is
+    one plausible size of the rounding effect, printed beside the gate.
+    """
+    q = np.asarray(qc, dtype=np.float64) * float(s_q)
+    k = np.asarray(kc, dtype=np.float64) * float(s_k)
+    v = np.asarray(vc, dtype=np.float64) * float(s_v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    group = Hq // Hkv
+    if rows is None:
+        rows = np.arange(Nq, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, Hq, rows.shape[0], d), dtype=np.float64)
+    _, lse = attention(q, k, v, scale, causal=causal, rows=rows)
+    vis = _visible(rows, Nq, Nk) if causal else None
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // group
+            S = scale * (q[b, h, rows, :] @ k[b, hk].T)
+            if vis is not None:
+                S = np.where(vis, S, -np.inf)
+            m = np.max(S, axis=1)
+            live = m > -np.inf
+            Pr = np.zeros_like(S)
+            Pr[live] = round_e4m3(np.exp(S[live] - m[live, None]))
+            z = np.sum(Pr, axis=1)
+            out[b, h, live] = (Pr[live] @ v[b, hk]) / z[live, None]
+    return out, lse
 
 
 # --------------------------------------------------------------------------

@@ -12,6 +12,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 
@@ -638,3 +639,52 @@ def test_backward_rows_without_keys_have_zero_gradient():
     g = rng.standard_normal((1, 1, 6, 3))
     dq, _, _ = oracle.attention_backward(q, k, v, g, 1.0, causal=True)
     assert np.all(dq[0, 0, :3] == 0) and np.any(dq[0, 0, 3:] != 0)
+
+
+# ---------------------------------------------------------------------------
+# Report-only fp8 diagnostic: P rounded to e4m3
+# ---------------------------------------------------------------------------
+def test_round_e4m3_matches_torch_cast():
+    """round_e4m3 equals torch's float8_e4m3fn conversion (a library
+    routine) on fp32 values: normals, subnormals, exact ties, the largest
+    finite value and zero."""
+    rng = np.random.default_rng(3)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 10.0,
+        rng.uniform(-2 ** -6, 2 ** -6, 5000),            # subnormal range
+        np.array([0.0, 448.0, -448.0, 2 ** -9, 3 * 2 ** -10, 1.0625,
+                  1.1875, 240.0, 440.0, 0.01171875]),
+    ]).astype(np.float32)
+    x = x[np.abs(x) <= 448.0]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_e4m3(x.astype(np.float64)), want)
+
+
+def test_p_e4m3_diagnostic_special_cases():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 2, 20, 16))
+    k = rng.standard_normal((1, 1, 30, 16))
+    v = rng.standard_normal((1, 1, 30, 16))
+    # weights that are a convex combination: V of all ones gives O = 1
+    o, _ = oracle.attention_fp8_p_e4m3(q, k, np.ones_like(v), 1.0, 1.0, 1.0,
+                                       0.3)
+    assert np.max(np.abs(o - 1.0)) < 1e-14
+    # scores whose exponentials are powers of two are not rounded at all:
+    # then the diagnostic equals the oracle
+    kk = np.zeros((1, 1, 4, 16))
+    kk[0, 0, :, 0] = [0.0, -1.0, -2.0, -3.0]
+    qq = np.zeros((1, 1, 3, 16))
+    qq[0, 0, :, 0] = math.log(2.0)
+    vv = rng.standard_normal((1, 1, 4, 16))
+    o1, l1 = oracle.attention_fp8_p_e4m3(qq, kk, vv, 1.0, 1.0, 1.0, 1.0)
+    o2, l2 = oracle.attention(qq, kk, vv, 1.0)
+    assert np.max(np.abs(o1 - o2)) < 1e-14 and np.array_equal(l1, l2)
+    # causal row 0 sees one key: O = V[0]
+    o3, _ = oracle.attention_fp8_p_e4m3(q[:, :1], k[:, :, :20], v[:, :, :20],
+                                        1.0, 1.0, 1.0, 0.25, causal=True)
+    assert np.max(np.abs(o3[0, 0, 0] - v[0, 0, 0])) < 1e-14
+    # and the rounding moves O by no more than the e4m3 step allows
+    o4, _ = oracle.attention_fp8_p_e4m3(q, k, v, 1.0, 1.0, 1.0, 0.25)
+    o5, _ = oracle.attention(q, k, v, 0.25)
+    bound = 2 * 2 ** -4 * np.max(np.abs(v))
+    assert 0 < np.max(np.abs(o4 - o5)) <= bound
