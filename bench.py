@@ -24,6 +24,16 @@ TFLOPS (algorithmic FLOPs: 4*d per visible (query, key) pair per query
 head; causal counts N(N+1)/2 pairs). The decode, fp8 and backward legs are
 reported in their own objects (GB/s of algorithmic KV bytes, TFLOPS; the
 backward counts 10*d FLOPs per visible pair: five products).
+
+Each compute leg states its fraction of the datasheet peak (quoted at
+2.4 GHz) and, after the timed region, the shader clock it holds under its
+own load (bench_clock.hip's probe on a side stream while the leg runs back
+to back) with the fraction of the peak scaled to that clock.
+
+cpu_baseline: the fp64 oracle on this host, before the GPU is touched: a
+pool of one worker per core (at most 16) with one BLAS thread each, over
+256-row blocks of the causal prefill (about 12 s of work) and every request
+of the paged decode; core count and CPU model are stated.
 """
 from __future__ import annotations
 
@@ -35,6 +45,8 @@ import os
 import statistics
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -73,6 +85,78 @@ def decode_bytes(di, Hkv, d, kv_elem_bytes=2):
     return kv + B * Hq * d * 2 * 2 + B * Hq * 4 + pages * 4
 
 
+class ClockProbe:
+    """The shader clock a kernel holds under its own load: bench_clock.so's
+    probe (one wave reading the shader-clock counter against the constant
+    100 MHz counter) runs on a side stream while the kernel is launched back
+    to back on the main stream. On this chip it agrees with the rocprofv3
+    GRBM_COUNT clock of the same kernel to within about 2 %. None when the
+    probe library has not been built."""
+
+    def __init__(self, stream):
+        import ctypes
+        import torch
+        self.ok = False
+        path = os.path.join(ROOT, "bench_clock.so")
+        try:
+            lib = ctypes.CDLL(path)
+            lib.bench_clock_probe.argtypes = [ctypes.c_void_p,
+                                              ctypes.c_ulonglong,
+                                              ctypes.c_void_p]
+            lib.bench_clock_probe.restype = ctypes.c_int
+            lib.bench_clock_wall_rate_khz.restype = ctypes.c_int
+            self.khz = lib.bench_clock_wall_rate_khz()
+            self.lib = lib
+            self.stream = stream
+            self.side = torch.cuda.Stream()        # default priority
+            self.out = torch.zeros(2, dtype=torch.int64, device="cuda:0")
+            self.ok = self.khz > 0
+        except OSError as e:
+            print(f"bench: no clock probe ({e})", file=sys.stderr)
+
+    def measure(self, fn, seconds=0.25):
+        """Mean shader clock (MHz) over `seconds` of fn() run back to back,
+        and the window's length in ms."""
+        import torch
+        if not self.ok:
+            return None, 0.0
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        done = torch.cuda.Event()
+        rc = self.lib.bench_clock_probe(self.out.data_ptr(),
+                                        int(seconds * self.khz * 1e3),
+                                        self.side.cuda_stream)
+        if rc != 0:
+            return None, 0.0
+        done.record(self.side)
+        while not done.query():
+            for _ in range(4):
+                fn()
+            self.stream.synchronize()
+        torch.cuda.synchronize()
+        cyc, ticks = self.out.tolist()
+        if ticks <= 0:
+            return None, 0.0
+        return cyc / ticks * self.khz / 1e3, ticks / self.khz
+
+
+DATASHEET_MHZ = 2400.0
+
+
+def _at_clock(achieved, peak, mhz, n):
+    """The fraction of the datasheet peak, and of the peak scaled to the
+    measured shader clock."""
+    d = {"clock_mhz": mhz, "clock_window_ms": n,
+         "clock_source": "shader-clock probe (bench_clock.hip) on a side "
+                         "stream while the kernel ran back to back, after "
+                         "the timed region"}
+    if mhz:
+        d["peak_at_clock"] = peak * mhz / DATASHEET_MHZ
+        d["frac_at_clock"] = achieved / d["peak_at_clock"]
+    return d
+
+
 def _launch_stats(samples):
     """Mean, median, min and max of one leg's per-launch times in ms."""
     return {"launch_ms_mean": statistics.mean(samples),
@@ -102,54 +186,141 @@ def _traffic(kernel_key, sources):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(target_s=12.0):
-    """The fp64 oracle timed on this host on a bounded sample of the causal
-    prefill workload: whole query heads (every row, every visible key)
-    sharing one KV head, as many as take about target_s seconds (the last R
-    rows of one head if even one head is slower than that)."""
-    import numpy as np
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# Arrays the CPU-baseline workers read: set before the pool forks, so every
+# worker inherits them and a task is only a pair of indices.
+_CPU = {}
+
+
+def _cpu_worker_init():
+    # one BLAS thread per worker (the environment was set before the pool
+    # started; this covers libraries that ignore it)
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # noqa: BLE001
+        pass
+
+
+def _cpu_ping(x):
+    return x
+
+
+def _cpu_prefill_item(task):
+    """The oracle on one block of query rows of one query head of the causal
+    prefill (with the head's whole K/V, as the oracle takes them)."""
     import oracle
+    h, j = task
+    q, k, v, G, R, scale = (_CPU[x] for x in ("q", "k", "v", "G", "R", "scale"))
+    rows = np.arange(j * R, (j + 1) * R)
+    t0 = time.perf_counter()
+    oracle.attention(q[h][None, None], k[h // G][None, None],
+                     v[h // G][None, None], scale, causal=True, rows=rows)
+    return time.perf_counter() - t0
+
+
+def _cpu_decode_item(r):
+    """The oracle's paged decode of request r."""
+    import oracle
+    d = _CPU["dec"]
+    t0 = time.perf_counter()
+    oracle.paged_decode(d["q"][r:r + 1], d["kp"], d["vp"], d["bt"][r:r + 1],
+                        d["sl"][r:r + 1], d["page"], d["scale"])
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(prefill_inp, decode_inp, target_s=12.0, rows=256):
+    """The fp64 oracle timed on this host's cores, on the same seeded arrays
+    the GPU legs use: a pool of one worker per core (at most 16: the host
+    share of one GPU), one BLAS thread each. Called before the GPU is
+    touched (the workers are forked from this process).
+
+    * prefill: blocks of `rows` query rows of the causal GQA prefill, spread
+      over heads and row positions (a block at every row offset, so the
+      causal work mix is the workload's), as many as take about target_s;
+      the rate counts the algorithmic FLOPs of the rows computed.
+    * decode: every request of the paged-decode workload, one task each;
+      the rate counts the algorithmic bytes (K/V once per KV head + q, o,
+      LSE, table entries), as the GPU figure does.
+    """
+    import multiprocessing as mp
+
+    import oracle  # noqa: F401  (imported before the fork: workers inherit it)
     import torch
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, 16))
     c = W.PREFILL_CONFIGS[PREFILL]
-    N, d = c["Nq"], c["d"]
-    scale = 1.0 / math.sqrt(d)
-
-    def draw(h):
-        rng = np.random.default_rng(42)
-        x = rng.standard_normal((1, h, N, d)).astype(np.float32)
-        return torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
-
-    q1, k, v = draw(1), draw(1), draw(1)
-    t0 = time.perf_counter()
-    oracle.attention(q1, k, v, scale, causal=True)
-    el = time.perf_counter() - t0
-    heads, rows = 1, N
-    if el > target_s:
-        rows = max(1, int(N * target_s / el))
+    N, d, Hq = c["Nq"], c["d"], c["Hq"]
+    _CPU.update(q=W.as_f64(prefill_inp.q)[0], k=W.as_f64(prefill_inp.k)[0],
+                v=W.as_f64(prefill_inp.v)[0], G=c["Hq"] // c["Hkv"], R=rows,
+                scale=prefill_inp.scale)
+    di = decode_inp
+    _CPU["dec"] = dict(q=W.as_f64(di.q),
+                       kp=di.k_pool.to(torch.float32).numpy(),
+                       vp=di.v_pool.to(torch.float32).numpy(),
+                       bt=di.block_table.numpy(), sl=di.seq_lens.numpy(),
+                       page=di.page_size, scale=di.scale)
+    saved = {k: os.environ.get(k) for k in
+             ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    pool = mp.get_context("fork").Pool(workers, initializer=_cpu_worker_init)
+    for k, val in saved.items():
+        if val is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = val
+    out = {"unit": "TFLOPS", "kind": "oracle", "cores": workers,
+           "affinity_cores": affinity, "cpu_model": _cpu_model(),
+           "blas_threads_per_worker": 1}
+    try:
+        pool.map(_cpu_ping, range(workers))   # every worker up before timing
+        nblk = N // rows
+        order = [(i % Hq, (i * 7) % nblk) for i in range(Hq * nblk)]
+        # rounds of one task per worker until target_s has passed (one
+        # untimed round first: page faults on the inherited arrays)
+        pool.map(_cpu_prefill_item, order[:workers], chunksize=1)
+        n_items, flops = 0, 0.0
         t0 = time.perf_counter()
-        oracle.attention(q1, k, v, scale, causal=True,
-                         rows=np.arange(N - rows, N))
+        while n_items < len(order) and time.perf_counter() - t0 < target_s:
+            tasks = order[n_items:n_items + workers]
+            pool.map(_cpu_prefill_item, tasks, chunksize=1)
+            n_items += len(tasks)
+            flops += sum(4.0 * d * float(np.sum(np.arange(j * rows, (j + 1) * rows) + 1))
+                         for _, j in tasks)
         el = time.perf_counter() - t0
-    elif el < target_s / 2:
-        heads = max(1, min(c["Hq"], int(round(target_s / max(el, 1e-3)))))
-        qh = draw(heads)
+        out.update({"value": flops / el / 1e12, "seconds": el,
+                    "sample": f"fp64 oracle on {n_items} blocks of {rows} "
+                              f"query rows of the causal GQA prefill N={N} "
+                              f"d={d} (every row offset; {flops / 1e9:.1f} "
+                              f"GFLOP in {el:.1f} s), {workers} workers x 1 "
+                              f"BLAS thread"})
+        nreq = di.q.shape[0]
+        nbytes = decode_bytes(di, di.k_pool.shape[2], di.k_pool.shape[3])
         t0 = time.perf_counter()
-        oracle.attention(qh, k, v, scale, causal=True)
+        pool.map(_cpu_decode_item, range(nreq), chunksize=1)
         el = time.perf_counter() - t0
-    flops = 4.0 * d * heads * sum(i + 1 for i in range(N - rows, N))
-    return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": threads,
-            "kind": "oracle",
-            "sample": f"fp64 oracle, {heads} query head(s) x last {rows} rows "
-                      f"of the causal N={N} d={d} GQA prefill "
-                      f"({flops / 1e9:.1f} GFLOP in {el:.1f} s)",
-            "seconds": el}
+        out["decode"] = {"value": nbytes / el / 1e9, "unit": "GB/s",
+                         "seconds": el,
+                         "sample": f"fp64 oracle paged decode of all {nreq} "
+                                   f"requests ({nbytes / 1e6:.1f} MB "
+                                   f"algorithmic), {workers} workers"}
+    finally:
+        pool.terminate()
+        pool.join()
+        _CPU.clear()
+    return out
 
 
 def main():
@@ -171,18 +342,34 @@ def main():
 
     import torch
     import workloads as W
-    import exact_attention_28_amd as fa
+    legs = [x for x in args.legs.split(",") if x]
 
+    # host inputs first; the CPU oracle baseline runs on them before the GPU
+    # is touched (its worker pool is forked from this process)
+    host = {}
+    if "prefill" in legs or "bwd" in legs:
+        host["prefill"] = W.prefill_config(PREFILL)
+    if "decode" in legs:
+        host["decode"] = W.decode_config(DECODE)
+    cpu = None
+    if not args.no_cpu_baseline and "prefill" in legs and "decode" in legs:
+        print("bench: timing the CPU oracle baseline", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(host["prefill"], host["decode"])
+        print(f"bench: CPU oracle {cpu['value'] * 1e3:.1f} GFLOP/s, decode "
+              f"{cpu['decode']['value']:.2f} GB/s", file=sys.stderr,
+              flush=True)
+
+    import exact_attention_28_amd as fa
     fa.load_library()
     dev = torch.device("cuda:0")
-    legs = [x for x in args.legs.split(",") if x]
     stream = torch.cuda.current_stream(dev)
 
     calls = {}
     info = {}
     if "prefill" in legs:
         c = W.PREFILL_CONFIGS[PREFILL]
-        inp = W.prefill_config(PREFILL)
+        inp = host["prefill"]
         q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
         o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -192,7 +379,7 @@ def main():
         info["prefill"] = dict(flops=prefill_flops(c), cfg=c)
     if "decode" in legs:
         c = W.DECODE_CONFIGS[DECODE]
-        di = W.decode_config(DECODE)
+        di = host["decode"]
         q = di.q.to(dev)
         kp, vp = di.k_pool.to(dev), di.v_pool.to(dev)
         bt, sl = di.block_table.to(dev), di.seq_lens.to(dev)
@@ -230,7 +417,7 @@ def main():
         # backward of the causal GQA prefill: O and LSE from one forward
         # call outside the timed region, dO seeded
         cb = W.PREFILL_CONFIGS[PREFILL]
-        ib = W.prefill_config(PREFILL)
+        ib = host["prefill"]
         qb, kb, vb = (t.to(dev) for t in (ib.q, ib.k, ib.v))
         gb = W.upstream_grad(tuple(ib.q.shape), seed=43).to(dev)
         ob = torch.empty(qb.shape, dtype=torch.bfloat16, device=dev)
@@ -346,6 +533,16 @@ def main():
         torch.cuda.synchronize()
         order = order + extra
     ms = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in order}
+    # the shader clock each kernel holds under its own load, sampled while
+    # it runs back to back (outside the timed region)
+    clock = {}
+    probe = ClockProbe(stream)
+    for name in order:
+        if name != "naive":
+            clock[name] = probe.measure(calls[name])
+    print("bench: clocks " + ", ".join(
+        f"{n}={c[0]:.0f}MHz" for n, c in clock.items() if c[0]),
+        file=sys.stderr, flush=True)
     print("bench: timed region done " + ", ".join(
         f"{n}={statistics.mean(ms[n]):.3f}ms" for n in order),
         file=sys.stderr, flush=True)
@@ -371,6 +568,7 @@ def main():
             # the pages' 3 softmax FLOPs per score, kept out of TFLOPS
             "softmax_gflop_per_launch": 0.75 * info["prefill"]["flops"]
             / c["d"] / 1e9,
+            **_at_clock(tf, PEAK_BF16_TFLOPS, *clock["prefill"]),
             **_launch_stats(ms["prefill"])}
         workload.append(f"bf16 causal GQA prefill B={c['B']} Hq={c['Hq']} "
                         f"Hkv={c['Hkv']} N={c['Nq']} d={c['d']}")
@@ -385,7 +583,10 @@ def main():
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS,
                          "traffic": _traffic("decode_r64",
-                                             ["fa_decode.hip", "fa_device.h"])},
+                                             ["fa_decode.hip", "fa_device.h"]),
+                         # HBM bandwidth does not scale with the shader
+                         # clock; the clock is reported for reference
+                         "clock_mhz": clock["decode"][0]},
             "algorithmic_bytes": info["decode"]["bytes"],
             "kv_tokens": info["decode"]["kv_tokens"],
             **_launch_stats(ms["decode"])}
@@ -400,6 +601,7 @@ def main():
         tf = info["fp8"]["flops"] / t / 1e12
         out["fp8_prefill"] = {
             "value": tf, "unit": "TFLOPS", "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
+            **_at_clock(tf, PEAK_FP8_TFLOPS, *clock["fp8"]),
             **_launch_stats(ms["fp8"])}
         workload.append(f"fp8 e4m3 prefill B={c['B']} H={c['Hq']} N={c['Nq']} "
                         f"d={c['d']}")
@@ -413,6 +615,7 @@ def main():
             "value": tf, "unit": "TFLOPS", "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
             "algorithmic_gflop_per_launch": info["bwd"]["flops"] / 1e9,
             "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel",
+            **_at_clock(tf, PEAK_BF16_TFLOPS, *clock["bwd"]),
             **_launch_stats(ms["bwd"])}
         workload.append(f"bf16 causal GQA backward B={c['B']} Hq={c['Hq']} "
                         f"Hkv={c['Hkv']} N={c['Nq']} d={c['d']}")
@@ -426,6 +629,7 @@ def main():
             "kernel": "decode_kernel<e4m3 cache> + decode_merge_kernel",
             "algorithmic_bytes": info["decode8"]["bytes"],
             "tokens_per_s": info["decode8"]["kv_tokens"] / t,
+            "clock_mhz": clock["decode8"][0],
             **_launch_stats(ms["decode8"])}
         workload.append("paged decode over an e4m3 cache (same requests)")
         if "value" not in out:
@@ -439,6 +643,8 @@ def main():
         heads = c["B"] * c["Hq"]
         N, d = c["Nq"], c["d"]
         entry = {"value": tf, "unit": "TFLOPS", **_launch_stats(ms[leg])}
+        if leg in clock:
+            entry["clock_mhz"] = clock[leg][0]
         if leg == "naive":
             # the pages' traffic ledger, 8Nd + 8N^2 bytes per head
             entry["ledger_bytes"] = heads * (8 * N * d + 8 * N * N)
@@ -456,7 +662,9 @@ def main():
         tf = info["chunked"]["flops"] / t / 1e12
         out["chunked_prefill"] = {
             "value": tf, "unit": "TFLOPS", "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
-            "kernel": "fwd_bf16_kernel<paged>", **_launch_stats(ms["chunked"])}
+            "kernel": "fwd_bf16_kernel<paged>",
+            **_at_clock(tf, PEAK_BF16_TFLOPS, *clock["chunked"]),
+            **_launch_stats(ms["chunked"])}
         workload.append("chunked prefill 16 requests x 512 new tokens, paged "
                         "cache U{4096..8192}, Hq=32 Hkv=8 d=128")
         if "value" not in out:
@@ -470,10 +678,8 @@ def main():
             out["value"], out["unit"] = info["copy"]["bytes"] / t / 1e9, "GB/s"
     out["config"] = {"workload": " + ".join(workload), "seed": 42,
                      "parallelism": "single GPU"}
-    if not args.no_cpu_baseline and "prefill" in order:
-        print("bench: timing the CPU oracle baseline", file=sys.stderr,
-              flush=True)
-        out["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -74,5 +74,24 @@ def build_library(verbose: bool = False) -> str:
     return OUT
 
 
+def build_clock_probe(verbose: bool = False) -> str:
+    """bench_clock.so next to bench.py: the shader-clock probe the
+    benchmark uses to state fractions of peak at the measured clock (not
+    part of libfa)."""
+    root = os.path.dirname(PKG)
+    src = os.path.join(root, "bench_clock.hip")
+    out = os.path.join(root, "bench_clock.so")
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), *FLAGS, "-shared", src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    os.replace(tmp, out)
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
     build_library(verbose=True)
+    build_clock_probe(verbose=True)
