@@ -158,35 +158,105 @@ def _sample_rows(N, rng, extra=48):
     return np.array(sorted(rows))
 
 
+def _rne_bf16(x):
+    """Round fp64 to the nearest bf16 value, ties to even (for the
+    rounding-only report; normal range)."""
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = np.exp2(e - 7)
+    return np.where(a > 0, np.round(x / ulp) * ulp, x)
+
+
+def _report(inp, o, ro, what, rows=None, sub=None):
+    """Report-only numbers printed beside the gate: for bf16 outputs the
+    error beyond the output's own rounding, max|O - RNE_bf16(O_ref)|; for
+    fp8 the oracle variant with P rounded to e4m3 (never a gate)."""
+    if inp.dtype == "bf16":
+        print(f"{what}: rounding-only report max|O - RNE_bf16(O_ref)| = "
+              f"{float(np.max(np.abs(o - _rne_bf16(ro)))):.3e}")
+    elif inp.dtype == "fp8":
+        src = sub if sub is not None else inp
+        do, _ = oracle.attention_fp8_p_e4m3(
+            W.as_f64(src.q), W.as_f64(src.k), W.as_f64(src.v), *src.descale,
+            src.scale, causal=src.causal, rows=rows)
+        print(f"{what}: P-e4m3 diagnostic (report only): "
+              f"max|O - O_ref|={float(np.max(np.abs(o - ro))):.3e} "
+              f"max|O - O_diag|={float(np.max(np.abs(o - do))):.3e} "
+              f"max|O_diag - O_ref|={float(np.max(np.abs(do - ro))):.3e}")
+
+
 @pytest.mark.parametrize("name", sorted(W.PREFILL_CONFIGS))
 def test_fwd_full_workload(fa, name):
+    """Full-size workloads: in full where the oracle takes seconds
+    (B*Hq*Nq*Nk <= 2^28 scores: the fp32 and the non-causal bf16 ones);
+    otherwise every (batch, head) on sampled rows, plus one head in full
+    (its rows in chunks)."""
     c = W.PREFILL_CONFIGS[name]
     inp = W.prefill_config(name)
     o, lse = _gpu_fwd(fa, inp)
-    if c["Nq"] * c["Nk"] * c["B"] * c["Hq"] <= (1 << 26):
+    if c["Nq"] * c["Nk"] * c["B"] * c["Hq"] <= (1 << 28):
         ro, rl = _oracle_fwd(inp)
-        _compare(o, lse, ro, rl, c["dtype"], name)
+        _compare(o, lse, ro, rl, c["dtype"], f"{name} (full)")
+        _report(inp, o, ro, name)
         return
     rng = np.random.default_rng(0)
     rows = _sample_rows(c["Nq"], rng)
-    # (batch, head) pairs: first and last head, a middle one, and the last
-    # head of the first GQA group
     G = c["Hq"] // c["Hkv"]
-    pairs = sorted({(0, 0), (0, c["Hq"] - 1), (c["B"] - 1, c["Hq"] // 2),
-                    (c["B"] - 1, G - 1)})
-    for b, h in pairs:
-        sub = W.PrefillInputs(inp.q[b:b + 1, h:h + 1], inp.k[b:b + 1, h // G:h // G + 1],
-                              inp.v[b:b + 1, h // G:h // G + 1], inp.scale,
-                              inp.causal, inp.dtype, inp.descale)
-        ro, rl = _oracle_fwd(sub, rows=rows)
-        _compare(o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows], ro, rl,
-                 c["dtype"], f"{name} b{b} h{h}")
+
+    def head(b, h):
+        return W.PrefillInputs(inp.q[b:b + 1, h:h + 1],
+                               inp.k[b:b + 1, h // G:h // G + 1],
+                               inp.v[b:b + 1, h // G:h // G + 1], inp.scale,
+                               inp.causal, inp.dtype, inp.descale)
+
+    ob, lb, rob, rlb = [], [], [], []
+    for b in range(c["B"]):
+        for h in range(c["Hq"]):
+            ro, rl = _oracle_fwd(head(b, h), rows=rows)
+            _compare(o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows],
+                     ro, rl, c["dtype"], f"{name} b{b} h{h} ({len(rows)} rows)")
+            ob.append(o[b:b + 1, h:h + 1, rows])
+            rob.append(ro)
+    if inp.dtype == "bf16":
+        _report(inp, np.concatenate(ob), np.concatenate(rob),
+                f"{name} sampled rows, all heads")
+    else:
+        # the diagnostic on the sampled rows of four heads
+        for b, h in ((0, 0), (0, c["Hq"] - 1), (c["B"] - 1, 0),
+                     (c["B"] - 1, c["Hq"] - 1)):
+            sub = head(b, h)
+            ro, _ = _oracle_fwd(sub, rows=rows)
+            _report(inp, o[b:b + 1, h:h + 1, rows], ro,
+                    f"{name} b{b} h{h} sampled rows", rows=rows, sub=sub)
+    # one head in full, 2048 rows at a time
+    b, h = c["B"] - 1, c["Hq"] - 1
+    sub = head(b, h)
+    worst = (0.0, 0.0)
+    for r0 in range(0, c["Nq"], 2048):
+        rr = np.arange(r0, min(c["Nq"], r0 + 2048))
+        ro, rl = _oracle_fwd(sub, rows=rr)
+        _compare(o[b:b + 1, h:h + 1, rr], lse[b:b + 1, h:h + 1, rr], ro, rl,
+                 c["dtype"], f"{name} b{b} h{h} rows {r0}..{rr[-1]}")
+        worst = (max(worst[0], float(np.max(np.abs(o[b, h, rr] - ro[0, 0])))),
+                 max(worst[1], float(np.max(np.abs(lse[b, h, rr] - rl[0, 0])))))
+    print(f"{name} b{b} h{h} in full: max|dO|={worst[0]:.3e} "
+          f"max|dLSE|={worst[1]:.3e}")
     # properties over every row: no NaN, causal row 0 of every head is V[0]
     assert not np.any(np.isnan(o)) and np.all(np.isfinite(lse))
     if inp.causal:
         v0 = W.as_f64(inp.v[:, :, 0])                       # [B, Hkv, d]
         want = np.repeat(v0, G, axis=1)
         assert np.max(np.abs(o[:, :, 0] - want)) <= 4e-3
+
+
+def test_api_rejects_non_contiguous_device_tensors(fa):
+    inp = W.prefill_inputs(1, 2, 2, 64, 64, 64, dtype="bf16")
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    with pytest.raises(fa.FaError, match="not contiguous"):
+        fa.attention(q.transpose(2, 3).contiguous().transpose(2, 3), k, v)
+    with pytest.raises(fa.FaError, match="not in GPU memory"):
+        fa.attention(q, k.cpu(), v)
 
 
 # ---------------------------------------------------------------- decode
