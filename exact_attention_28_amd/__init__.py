@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     fa_naive_workspace_size,
     fa_paged_decode,
     fa_paged_decode_fp8kv,
+    fa_paged_decode_noalloc,
     fa_paged_decode_workspace_size,
     fa_paged_prefill,
     fa_strerror,

@@ -29,11 +29,13 @@ FA_EPAGE = -8
 FA_EWORKSPACE = -9
 FA_ESPLITS = -10
 FA_EALIGN = -11
+FA_ESCRATCH = -12
 
 # every function include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_naive_attention",
            "fa_naive_workspace_size", "fa_paged_decode",
-           "fa_paged_decode_fp8kv", "fa_paged_decode_workspace_size",
+           "fa_paged_decode_fp8kv", "fa_paged_decode_noalloc",
+           "fa_paged_decode_workspace_size",
            "fa_paged_prefill", "fa_strerror")
 
 
@@ -72,6 +74,9 @@ def load_library(path: str = LIB_PATH):
     lib.fa_naive_attention.argtypes = [vp] * 5 + [i] * 6 + [f, i, vp, sz, vp]
     lib.fa_naive_workspace_size.restype = sz
     lib.fa_naive_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_paged_decode_noalloc.restype = i
+    lib.fa_paged_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i,
+                                            i, i, i, f, vp, vp, i, vp]
     lib.fa_paged_decode_fp8kv.restype = i
     lib.fa_paged_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i,
                                           i, i, f, vp, vp, vp, vp, sz, i, vp]
@@ -170,6 +175,23 @@ def fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, page_size,
         int(Hkv), int(d), int(max_pages_per_seq), float(scale), _ptr(o),
         _ptr(lse), _ptr(workspace), int(workspace_bytes), int(num_splits),
         _stream(stream, q, o))
+    if check:
+        _check(code)
+    return code
+
+
+def fa_paged_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens,
+                            page_size, num_pages, B, Hq, Hkv, d,
+                            max_pages_per_seq, scale, o, lse, num_splits=0,
+                            stream=None, check=True) -> int:
+    """Paged-KV decode with the library's built-in workspace (see
+    include/fa.h): nothing is allocated by the call."""
+    lib = load_library()
+    code = lib.fa_paged_decode_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        _ptr(seq_lens), int(page_size), int(num_pages), int(B), int(Hq),
+        int(Hkv), int(d), int(max_pages_per_seq), float(scale), _ptr(o),
+        _ptr(lse), int(num_splits), _stream(stream, q, o))
     if check:
         _check(code)
     return code

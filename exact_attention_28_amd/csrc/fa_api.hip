@@ -50,6 +50,7 @@ const char* fa_strerror(int code) {
     case FA_EWORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ESPLITS: return "num_splits is negative or above 65536";
     case FA_EALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FA_ESCRATCH: return "the decode needs more than the library's built-in 16 MiB workspace for these sizes";
     default: break;
   }
   if (code > 0) return "HIP launch error (the value is a hipError_t)";
@@ -296,7 +297,7 @@ static int paged_decode_common(const void* q, const void* k_pool,
                                float* lse, void* workspace,
                                size_t workspace_bytes, int num_splits,
                                bool kv_fp8, float s_k, float s_v,
-                               void* stream) {
+                               void* stream, bool use_scratch = false) {
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o)
     return FA_EINVAL_NULL;
   const int c = decode_check(B, Hq, Hkv, d, max_pages_per_seq, page_size,
@@ -312,9 +313,25 @@ static int paged_decode_common(const void* q, const void* k_pool,
   fa::DecodePlan plan;
   if (!fa::plan_decode(B, Hq, Hkv, d, max_pages_per_seq, num_splits, &plan))
     return FA_ESPLITS;
-  if (!workspace || workspace_bytes < plan.workspace_bytes ||
-      ((uintptr_t)workspace & 255u) != 0)
+  if (use_scratch) {
+    // the built-in workspace: an automatic range count is lowered until the
+    // plan fits it; a count the caller chose must fit as it is
+    if (plan.workspace_bytes > fa::kDecodeScratchBytes) {
+      if (num_splits != 0) return FA_ESCRATCH;
+      const long rows = ((long)(fa::kDecodeScratchBytes / 4) - plan.off_o) /
+                        ((long)Hq * (d + 1));
+      const long r_max = (rows - B) / plan.waves_per_head * plan.waves_per_head;
+      if (r_max < plan.waves_per_head) return FA_ESCRATCH;
+      if (!fa::plan_decode(B, Hq, Hkv, d, max_pages_per_seq, (int)r_max, &plan) ||
+          plan.workspace_bytes > fa::kDecodeScratchBytes)
+        return FA_ESCRATCH;
+    }
+    const hipError_t e = fa::decode_scratch(&workspace);
+    if (e != hipSuccess) return (int)e;
+  } else if (!workspace || workspace_bytes < plan.workspace_bytes ||
+             ((uintptr_t)workspace & 255u) != 0) {
     return FA_EWORKSPACE;
+  }
 
   fa::DecodeArgs a;
   a.q = q;
@@ -350,6 +367,18 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                              max_pages_per_seq, scale, o, lse, workspace,
                              workspace_bytes, num_splits, false, 1.f, 1.f,
                              stream);
+}
+
+int fa_paged_decode_noalloc(const void* q, const void* k_pool,
+                            const void* v_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, int page_size,
+                            int num_pages, int B, int Hq, int Hkv, int d,
+                            int max_pages_per_seq, float scale, void* o,
+                            float* lse, int num_splits, void* stream) {
+  return paged_decode_common(q, k_pool, v_pool, block_table, seq_lens,
+                             page_size, num_pages, B, Hq, Hkv, d,
+                             max_pages_per_seq, scale, o, lse, nullptr, 0,
+                             num_splits, false, 1.f, 1.f, stream, true);
 }
 
 int fa_paged_decode_fp8kv(const void* q, const void* k_pool,

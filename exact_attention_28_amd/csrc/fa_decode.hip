@@ -40,10 +40,19 @@
 //   * O[head, d] += P V on the VALU: a lane owns 4 tokens and D/16 d
 //     columns, P is broadcast inside each 16-lane row with DPP
 //     row_newbcast, V is read 16 B per lane from HBM.
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.h"
 #include "fa_kernels.h"
+
+// Built-in workspace of the decode for callers that cannot allocate device
+// memory (fa_paged_decode_noalloc): every device the library runs on holds
+// one copy of this array for the life of the process. Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in
+// for the symbol); it uses the device address that decode_scratch() looks
+// up once per device.
+static __device__ __align__(256) unsigned char scratch[fa::kDecodeScratchBytes];
 
 namespace fa {
 namespace {
@@ -559,6 +568,26 @@ int resident_waves(void* kernel, int nw) {
 }
 
 }  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static void* addr[kMaxDevices] = {};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p & 255u) != 0) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 bool plan_decode(int B, int Hq, int Hkv, int d, int max_pages, int num_splits,
                  DecodePlan* p) {

@@ -95,4 +95,11 @@ bool plan_decode(int B, int Hq, int Hkv, int d, int max_pages,
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan);
 
+// Size of the decode's built-in workspace (one per device, for the entry
+// point that allocates nothing), and its device address on the current
+// device: looked up with hipGetSymbolAddress on the first call per device,
+// then reused. Returns the lookup's error, if any.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace fa

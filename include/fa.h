@@ -11,6 +11,8 @@
  *                    LSE, with P re-computed on chip (never stored).
  *   fa_paged_decode  one query token per request against a paged KV cache,
  *                    split over workgroups and merged by log-sum-exp.
+ *   fa_paged_decode_noalloc  the same with the library's built-in
+ *                    workspace, for callers that cannot allocate.
  *   fa_paged_decode_fp8kv  the same over a cache stored as e4m3 codes with
  *                    per-tensor scales (half the bytes to read).
  *   fa_paged_prefill chunked prefill: a block of new query tokens per
@@ -36,7 +38,9 @@
  *   allocated and owned by the caller, contiguous in the layout stated,
  *   16-byte aligned (4-byte for fp32 LSE and the int32 tables).
  *   The library never allocates, frees or keeps a pointer, and keeps no
- *   state between calls: calls from several host threads are safe.
+ *   state between calls: calls from several host threads are safe. (The
+ *   one exception, fa_paged_decode_noalloc, uses a workspace built into the
+ *   library and documents the rules that come with it.)
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *   stream) and runs asynchronously: outputs are valid once the stream has
  *   reached the call. Nothing inside synchronises with the host, allocates
@@ -86,6 +90,8 @@ extern "C" {
 #define FA_ESPLITS (-10)        /* num_splits < 0 or > 65536                */
 #define FA_EALIGN (-11)         /* a tensor pointer is not 16-byte aligned
                                    (4-byte for lse, block_table, seq_lens) */
+#define FA_ESCRATCH (-12)       /* fa_paged_decode_noalloc: the sizes need
+                                   more than the built-in workspace        */
 
 /*
  * fa_fwd - exact attention forward, prefill / training shape.
@@ -225,6 +231,38 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                     int d, int max_pages_per_seq, float scale, void* o,
                     float* lse, void* workspace, size_t workspace_bytes,
                     int num_splits, void* stream);
+
+/*
+ * fa_paged_decode_noalloc - fa_paged_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. It calls no allocating routine;
+ * the split partials live in a workspace built into the library instead of
+ * a caller buffer: a 16 MiB array that every device the library runs on
+ * holds once, from the first call on that device until the process ends.
+ *
+ * Arguments, results and errors as fa_paged_decode, without `workspace`
+ * and `workspace_bytes`, plus:
+ * num_splits   0 = auto: the range count fa_paged_decode would choose,
+ *              lowered (to a multiple of the ranges one workgroup holds)
+ *              until the partials fit the built-in workspace; the result is
+ *              the same up to fp32 rounding. An explicit count whose
+ *              partials do not fit -> FA_ESCRATCH.
+ * FA_ESCRATCH  the sizes need more than the built-in workspace even with
+ *              the fewest ranges (about (B + ranges) * Hq * (d + 1) * 4
+ *              bytes must fit in 16 MiB).
+ * All calls on one device share its built-in workspace, which keeps the
+ * last call's contents (a call never reads what an earlier call left):
+ * calls that may run at the same time on one device (from different
+ * streams or host threads) race on it and must be serialised by the
+ * caller. A positive return is also possible from the first call on a
+ * device, when the workspace's device address cannot be looked up.
+ */
+int fa_paged_decode_noalloc(const void* q, const void* k_pool,
+                            const void* v_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, int page_size,
+                            int num_pages, int B, int Hq, int Hkv, int d,
+                            int max_pages_per_seq, float scale, void* o,
+                            float* lse, int num_splits, void* stream);
 
 /*
  * fa_paged_decode_fp8kv - fa_paged_decode over a KV cache stored as OCP

@@ -293,3 +293,31 @@ def ppf(**kw):
 ])
 def test_paged_prefill_rejects(lib, kw, code):
     assert ppf(**kw) == code
+
+
+def dec_na(**kw):
+    a = dict(q=P, k_pool=P, v_pool=P, block_table=P, seq_lens=P, page_size=16,
+             num_pages=100, B=4, Hq=32, Hkv=8, d=128, max_pages_per_seq=512,
+             scale=0.1, o=P, lse=P, num_splits=0, stream=None)
+    a.update(kw)
+    return fa.fa_paged_decode_noalloc(**a, check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), L.FA_EINVAL_NULL),
+    (dict(o=None), L.FA_EINVAL_NULL),
+    (dict(B=0), L.FA_EINVAL_DIM),
+    (dict(d=96), L.FA_EUNSUPPORTED_D),
+    (dict(Hq=12, Hkv=8), L.FA_EGQA),
+    (dict(page_size=8), L.FA_EPAGE),
+    (dict(num_splits=-1), L.FA_ESPLITS),
+    (dict(scale=float("nan")), L.FA_ESCALE),
+    (dict(k_pool=P + 4), L.FA_EALIGN),
+    # an explicit range count whose partials exceed the 16 MiB built-in
+    # workspace: (4 + 4096) * 32 * 129 * 4 bytes
+    (dict(num_splits=4096), L.FA_ESCRATCH),
+    # so many requests that even one range per KV head does not fit
+    (dict(B=2000, max_pages_per_seq=64), L.FA_ESCRATCH),
+])
+def test_decode_noalloc_rejects(lib, kw, code):
+    assert dec_na(**kw) == code
