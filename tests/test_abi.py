@@ -321,3 +321,94 @@ def dec_na(**kw):
 ])
 def test_decode_noalloc_rejects(lib, kw, code):
     assert dec_na(**kw) == code
+
+
+# The prototypes of include/fa.h, parameter by parameter. The first
+# parameters of fa_fwd and fa_paged_decode are the boundary's fixed prefixes
+# fa_fwd(q,k,v,o,lse,B,Hq,Hkv,Nq,Nk,d,scale,causal) and
+# fa_paged_decode(q,k_pool,v_pool,block_table,seq_lens,page_size,...);
+# what follows them (and the decode workspace query's Hkv) are the
+# library's own choices.
+PROTOTYPES = {
+    "fa_fwd": ("int", [
+        "const void* q", "const void* k", "const void* v", "void* o",
+        "float* lse", "int B", "int Hq", "int Hkv", "int Nq", "int Nk",
+        "int d", "float scale", "int causal", "int dtype",
+        "const float* qkv_descale", "void* stream"]),
+    "fa_bwd_workspace_size": ("size_t", ["int B", "int Hq", "int Nq"]),
+    "fa_bwd": ("int", [
+        "const void* q", "const void* k", "const void* v", "const void* o",
+        "const void* dout", "const float* lse", "void* dq", "void* dk",
+        "void* dv", "int B", "int Hq", "int Hkv", "int Nq", "int Nk", "int d",
+        "float scale", "int causal", "int dtype", "void* workspace",
+        "size_t workspace_bytes", "void* stream"]),
+    "fa_paged_decode_workspace_size": ("size_t", [
+        "int B", "int Hq", "int Hkv", "int d", "int max_pages_per_seq",
+        "int page_size", "int num_splits"]),
+    "fa_paged_decode": ("int", [
+        "const void* q", "const void* k_pool", "const void* v_pool",
+        "const int32_t* block_table", "const int32_t* seq_lens",
+        "int page_size", "int num_pages", "int B", "int Hq", "int Hkv",
+        "int d", "int max_pages_per_seq", "float scale", "void* o",
+        "float* lse", "void* workspace", "size_t workspace_bytes",
+        "int num_splits", "void* stream"]),
+    "fa_paged_decode_noalloc": ("int", [
+        "const void* q", "const void* k_pool", "const void* v_pool",
+        "const int32_t* block_table", "const int32_t* seq_lens",
+        "int page_size", "int num_pages", "int B", "int Hq", "int Hkv",
+        "int d", "int max_pages_per_seq", "float scale", "void* o",
+        "float* lse", "int num_splits", "void* stream"]),
+    "fa_paged_decode_fp8kv": ("int", [
+        "const void* q", "const void* k_pool", "const void* v_pool",
+        "const int32_t* block_table", "const int32_t* seq_lens",
+        "int page_size", "int num_pages", "int B", "int Hq", "int Hkv",
+        "int d", "int max_pages_per_seq", "float scale",
+        "const float* kv_descale", "void* o", "float* lse", "void* workspace",
+        "size_t workspace_bytes", "int num_splits", "void* stream"]),
+    "fa_paged_prefill": ("int", [
+        "const void* q", "const void* k_pool", "const void* v_pool",
+        "const int32_t* block_table", "const int32_t* seq_lens",
+        "int page_size", "int num_pages", "int B", "int Hq", "int Hkv",
+        "int Nq", "int d", "int max_pages_per_seq", "float scale",
+        "int causal", "void* o", "float* lse", "void* stream"]),
+    "fa_naive_workspace_size": ("size_t", [
+        "int B", "int Hq", "int Nq", "int Nk"]),
+    "fa_naive_attention": ("int", [
+        "const void* q", "const void* k", "const void* v", "void* o",
+        "float* lse", "int B", "int Hq", "int Hkv", "int Nq", "int Nk",
+        "int d", "float scale", "int causal", "void* workspace",
+        "size_t workspace_bytes", "void* stream"]),
+    "fa_strerror": ("const char*", ["int code"]),
+}
+
+
+def _header_prototypes():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for ret, name, params in re.findall(
+            r"(const char\s*\*|size_t|int)\s+(fa_\w+)\s*\(([^;]*?)\)\s*;",
+            src, flags=re.S):
+        plist = [re.sub(r"\s+", " ", p.strip()).replace(" *", "*")
+                 for p in params.split(",")]
+        out[name] = (re.sub(r"\s+", "", ret).replace("char*", "char*")
+                     .replace("constchar*", "const char*"), plist)
+    return out
+
+
+def test_header_prototypes():
+    got = _header_prototypes()
+    assert sorted(got) == sorted(PROTOTYPES)
+    for name, (ret, params) in PROTOTYPES.items():
+        assert got[name] == (ret, params), name
+    # the fixed prefixes of the boundary
+    assert [p.split()[-1] for p in got["fa_fwd"][1][:13]] == [
+        "q", "k", "v", "o", "lse", "B", "Hq", "Hkv", "Nq", "Nk", "d", "scale",
+        "causal"]
+    assert [p.split()[-1] for p in got["fa_paged_decode"][1][:6]] == [
+        "q", "k_pool", "v_pool", "block_table", "seq_lens", "page_size"]
+
+
+def test_binding_argument_counts(lib):
+    for name, (_, params) in PROTOTYPES.items():
+        assert len(getattr(lib, name).argtypes) == len(params), name
