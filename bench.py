@@ -329,6 +329,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-seconds", type=float, default=0.25,
+                    help="seconds of back-to-back launches per leg for the "
+                    "shader-clock probe after the timed region (0: skip, "
+                    "for profiling runs)")
     ap.add_argument("--legs",
                     default="prefill,decode,fp8,bwd,decode8,noncausal,naive,"
                     "chunked",
@@ -535,11 +539,12 @@ def main():
     ms = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in order}
     # the shader clock each kernel holds under its own load, sampled while
     # it runs back to back (outside the timed region)
-    clock = {}
-    probe = ClockProbe(stream)
-    for name in order:
-        if name != "naive":
-            clock[name] = probe.measure(calls[name])
+    clock = {n: (None, 0.0) for n in order}
+    if args.clock_seconds > 0:
+        probe = ClockProbe(stream)
+        for name in order:
+            if name != "naive":
+                clock[name] = probe.measure(calls[name], args.clock_seconds)
     print("bench: clocks " + ", ".join(
         f"{n}={c[0]:.0f}MHz" for n, c in clock.items() if c[0]),
         file=sys.stderr, flush=True)
