@@ -44,6 +44,28 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 
+// Direct global->LDS loads (16 or 4 bytes per lane) written out as
+// instructions. The loops below read LDS while their next tile's direct
+// loads are in flight; a direct load issued through the compiler's builtin
+// counts there as an LDS access of unknown order, and the compiler then
+// waits for every outstanding LDS read (lgkmcnt 0) wherever it needs one,
+// so no fragment read can run ahead of the products that use it. Issued
+// this way the loads are invisible to its wait counting: the kernels wait
+// for them themselves (wait_vm0 before the barrier that publishes a tile),
+// and the waits the compiler computes for its own loads can only become
+// more conservative. M0 carries the wave's LDS base; the s_nop is the one
+// wait state a direct load needs after M0 is written.
+__device__ __forceinline__ void g2lds_16B_own(const void* g, lds_char* l) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0)
+               : "memory");
+}
+__device__ __forceinline__ void g2lds_4B_own(const void* g, lds_char* l) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0)
+               : "memory");
+}
+
 // A row-major tile of ROWS rows x D bf16 in LDS, as 1 KB blocks (one direct
 // load instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B. RowTile
 // below and IlvTile (the interleaved layout, fa_device.h) share one
@@ -92,7 +114,7 @@ __device__ __forceinline__ void load_tile(const __bf16* src, int r0, int n,
   for (int i = 0; i < T::BPW; ++i) {
     const int b = w + kWaves * i;
     const int r = min(r0 + T::block_row(b, lane), n - 1);
-    g2lds_16B(src + (long)r * D + 8 * chunk, dst + b * T::PITCH);
+    g2lds_16B_own(src + (long)r * D + 8 * chunk, dst + b * T::PITCH);
   }
 }
 
@@ -234,8 +256,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       // padding the prep kernel fills (masked either way, and finite or
       // +inf L2 with finite D, so P and dS come out exactly 0)
       const float* src = (lane < 32 ? L2 : Dv) + qb + BR * t + (lane & 31);
-      __builtin_amdgcn_global_load_lds(
-          src, (__attribute__((address_space(3))) void*)sbuf(buf), 4, 0, 0);
+      g2lds_4B_own(src, sbuf(buf));
     }
   };
 
