@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
     const float* __restrict__ Dv, const float* __restrict__ L2,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int B, int Hq, int Hkv,
-    int Nq, int Nk, float c, float scale) {
+    int Nq, int Nk, float c, float scale, int slots) {
   constexpr int BR = 32;  // query rows per tile
   using T = TrTile<D, BR>;      // Q, dO: read by rows and transposed
   using TV = RowTile<D, 128>;   // V: read by rows only
@@ -242,10 +242,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const int t0 = CAUSAL ? min(nqt, max(0, k0 - off) / BR) : 0;
   const int per_head = nqt - t0;
   const int n_it = G * per_head;
+  // Walk direction. The workgroups of an XCD run `slots` at a time, in
+  // dispatch order, heaviest first. Those of the first round start
+  // together at the last query tile and walk down abreast. Each slot then
+  // takes the next workgroup as its previous one ends, and the earlier a
+  // slot frees, the longer its next workgroup: walking up from its first
+  // visible tile, that round moves abreast as well (every slot reaches a
+  // given tile at about the same time), so one fetch of a tile serves the
+  // whole round from L2. Rounds alternate; without the causal mask all
+  // workgroups are equally long and walk down.
+  const int round = __builtin_amdgcn_readfirstlane((int)(blockIdx.x >> 3) / slots);
+  const bool up = CAUSAL && (round & 1);
+  const int tstart = up ? t0 : nqt - 1, tstep = up ? 1 : -1;
 
   // iteration it takes head g = it % G of the group and query tile
-  // t = nqt - 1 - it / G; (g, t) are carried from one iteration to the
-  // next instead of divided out
+  // t = tstart + tstep * (it / G); (g, t) are carried from one iteration
+  // to the next instead of divided out
   auto issue = [&](int g, int t, auto buf) {
     const long qb = (long)(ti.b * Hq + hk * G + g) * Nq;
     load_tile<D, T>(Q + qb * D, BR * t, Nq, qbuf(buf), w, lane);
@@ -272,8 +284,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
   constexpr std::integral_constant<int, 0> B0{};
   constexpr std::integral_constant<int, 1> B1{};
-  if (n_it > 0) issue(0, nqt - 1, B0);
-  int cg = 0, ct = nqt - 1;  // (g, t) of the current iteration
+  if (n_it > 0) issue(0, tstart, B0);
+  int cg = 0, ct = tstart;  // (g, t) of the current iteration
 
   auto step = [&](int it, auto par) {
     constexpr int P = decltype(par)::value;
@@ -284,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     wait_vm0();
     __syncthreads();
     int ng = cg + 1, nt = ct;
-    if (ng == G) { ng = 0; --nt; }
+    if (ng == G) { ng = 0; nt += tstep; }
     if (it + 1 < n_it) issue(ng, nt, nxt);
     const int t = ct;
     cg = ng;
@@ -400,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
     const float* __restrict__ Dv, const float* __restrict__ L2,
     __bf16* __restrict__ dQ, int B, int Hq, int Hkv, int Nq, int Nk, float c,
-    float scale) {
+    float scale, int slots) {
   constexpr int BN = 64;  // keys per tile
   using T = TrTile<D, BN>;  // K read by rows and transposed; V by rows
   __shared__ __attribute__((aligned(16))) char k_lds0[T::BYTES];
@@ -480,10 +492,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   auto skip_tile = [&](int tile) {
     return CAUSAL && (tile * BN > wrow0 + 31 + off);
   };
+  // Walk direction over the key tiles (see the dK/dV kernel): the first
+  // round of an XCD's workgroups starts together and walks up from key 0;
+  // the next round, whose workgroups start one by one as the longest
+  // before them end, walks down from its last visible tile and so stays
+  // abreast; rounds alternate.
+  const int round = __builtin_amdgcn_readfirstlane((int)(blockIdx.x >> 3) / slots);
+  const bool down = CAUSAL && (round & 1);
+  auto tile_at = [&](int it) { return down ? nt - 1 - it : it; };
 
   constexpr std::integral_constant<int, 0> B0{};
   constexpr std::integral_constant<int, 1> B1{};
-  if (nt > 0) issue(0, B0);
+  if (nt > 0) issue(tile_at(0), B0);
 
   auto step = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
@@ -491,9 +511,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     constexpr std::integral_constant<int, 1 - P> nxt{};
     wait_vm0();
     __syncthreads();
-    if (t + 1 < nt) issue(t + 1, nxt);
-    if (skip_tile(t)) return;
-    const int n0 = t * BN;
+    if (t + 1 < nt) issue(tile_at(t + 1), nxt);
+    const int tl = tile_at(t);
+    if (skip_tile(tl)) return;
+    const int n0 = tl * BN;
     const lds_char* kp = kbuf(cur);
     const lds_char* vp = vbuf(cur);
     // S^T = K Q^T, dP^T = V dO^T: lane = row r32, keys 32kb + 8(v/4) + 4h + v%4
@@ -582,6 +603,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 // (32 rows) of padding that the last tile of the last head may read.
 long bwd_rows_padded(long rows) { return (rows + 32 + 63) / 64 * 64; }
 
+// Workgroups of the dK/dV or dQ kernel that one XCD of the current device
+// runs at once: both kernels fit two workgroups on a CU (two waves per
+// SIMD by their launch bounds, 66 KB of LDS each), and the tile maps
+// spread the grid over the 8 XCDs.
+int slots_per_xcd() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess)
+    cus = 256;
+  return max(1, cus * 2 / 8);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {
   const long rows = (long)a.B * a.Hq * a.Nq;
@@ -602,7 +636,8 @@ hipError_t launch(const BwdArgs& a) {
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dout),
                      Dv, L2, static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv),
-                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, c, a.scale);
+                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, c, a.scale,
+                     slots_per_xcd());
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long q_blocks = (long)((a.Nq + 127) / 128) * a.Hq * a.B;
@@ -611,7 +646,8 @@ hipError_t launch(const BwdArgs& a) {
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dout),
                      Dv, L2, static_cast<__bf16*>(a.dq), a.B, a.Hq, a.Hkv, a.Nq,
-                     a.Nk, c, a.scale);
+                     a.Nk, c, a.scale,
+                     slots_per_xcd());
   return hipGetLastError();
 }
 
