@@ -82,6 +82,14 @@ def test_backward_matches_oracle(fa, B, Hq, Hkv, Nq, Nk, d, causal):
     _check(out, ref, f"bwd {B}x{Hq}/{Hkv}x{Nq}x{Nk}x{d} causal={causal}")
 
 
+def test_backward_several_dispatch_rounds(fa):
+    # more workgroups than the GPU runs at once (dK/dV: 1024 of 128 keys,
+    # dQ: 2048 of 128 rows, both two to a CU), so the later dispatch rounds
+    # walk their tiles the other way; every gradient compared in full
+    out, ref = _run(fa, 16, 32, 16, 512, 512, 128, True, seed=31)
+    _check(out, ref, "bwd 16x32/16x512x512x128 causal, several rounds")
+
+
 def test_backward_rows_without_keys_are_zero(fa):
     out, ref = _run(fa, 1, 2, 2, 300, 96, 64, True, seed=5)
     dq = out[0]
