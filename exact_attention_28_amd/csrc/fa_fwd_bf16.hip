@@ -200,6 +200,23 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
     koff[i] = k_row(w + kWaves * i) * D + 8 * chunk;
     voff[i] = v_row(w + kWaves * i) * D + 8 * chunk;
   }
+  // Paged cache, full tiles: a tile is 4 whole pages, so each of this
+  // lane's rows lies in a fixed page of the tile at a fixed offset inside
+  // it; per tile only the page ids change. The page's element offset is
+  // one 32 x 32 -> 64-bit multiply (ids are checked non-negative).
+  int kpg[T::BPW], kpo[T::BPW], vpg[T::BPW], vpo[T::BPW];
+  const uint32_t page_elems = 16u * (uint32_t)tok_stride;
+#pragma unroll
+  for (int i = 0; i < T::BPW; ++i) {
+    const int rk = k_row(w + kWaves * i), rv = v_row(w + kWaves * i);
+    kpg[i] = rk >> 4;
+    kpo[i] = (rk & 15) * (int)tok_stride + 8 * chunk;
+    vpg[i] = rv >> 4;
+    vpo[i] = (rv & 15) * (int)tok_stride + 8 * chunk;
+  }
+  auto page_off = [&](int n0, int pg) -> long {
+    return (long)((uint64_t)(uint32_t)page_ids[(n0 >> 4) + pg] * page_elems);
+  };
   // element offset of tile-relative row r of tile n0 (rows past the keys
   // clamped to the last key: their scores are masked, their P is 0)
   auto row_elem = [&](int n0, int r) -> long {
@@ -212,7 +229,11 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   auto issue_k = [&](int tile, auto buf) {
     const int n0 = tile * kBN;
     lds_char* dst = kbuf(buf) + w * T::KPITCH;
-    if (!PAGED && n0 + kBN <= nk) {
+    if (PAGED && n0 + kBN <= nk) {
+#pragma unroll
+      for (int i = 0; i < T::BPW; ++i)
+        g2lds_16B(Kh + page_off(n0, kpg[i]) + kpo[i], dst + kWaves * i * T::KPITCH);
+    } else if (!PAGED && n0 + kBN <= nk) {
       const __bf16* src = Kh + (long)n0 * D;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
@@ -227,7 +248,11 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
   auto issue_v = [&](int tile, auto buf) {
     const int n0 = tile * kBN;
     lds_char* dst = vbuf(buf) + w * T::VPITCH;
-    if (!PAGED && n0 + kBN <= nk) {
+    if (PAGED && n0 + kBN <= nk) {
+#pragma unroll
+      for (int i = 0; i < T::BPW; ++i)
+        g2lds_16B(Vh + page_off(n0, vpg[i]) + vpo[i], dst + kWaves * i * T::VPITCH);
+    } else if (!PAGED && n0 + kBN <= nk) {
       const __bf16* src = Vh + (long)n0 * D;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
