@@ -16,8 +16,8 @@ One step = one pass of the whole path over its synthetic workloads:
 Inputs are seeded N(0,1) draws (seed 42) already resident in HBM when the
 timed region starts. Each launch is bracketed by HIP events on the stream
 it runs on; the step time is the wall time of K steps of legs 1-3 between
-two device synchronisations. Legs 4-7 are timed afterwards, K launches
-each.
+two device synchronisations. Legs 5-7 are timed afterwards in a phase of
+their own, K launches each, and leg 4 (the backward) last, in another.
 
 Prints ONE JSON line. `value` is the bf16 causal prefill throughput in
 TFLOPS (algorithmic FLOPs: 4*d per visible (query, key) pair per query
@@ -501,12 +501,13 @@ def main():
     torch.cuda.synchronize()
     print(f"bench: inputs resident, legs={legs}", file=sys.stderr, flush=True)
 
-    # the step: the forward hot path (prefill, decode, fp8); the backward
-    # leg is timed after it in a phase of its own, so its heat and power
-    # draw do not change the clocks the forward legs run at
+    # the step: the forward hot path (prefill, decode, fp8). The other
+    # forward legs are timed after it in a phase of their own, and the
+    # backward last, in another: its heat and power draw (and the caches it
+    # leaves behind) do not change what the forward legs run at
     order = [x for x in ("prefill", "decode", "fp8", "copy") if x in calls]
-    extra = [x for x in ("bwd", "decode8", "noncausal", "naive", "chunked")
-             if x in calls]
+    phases = [[x for x in ("decode8", "noncausal", "naive", "chunked")
+               if x in calls], [x for x in ("bwd",) if x in calls]]
 
     def timed(names, steps):
         ev = {n: [] for n in names}
@@ -528,7 +529,9 @@ def main():
     ev = timed(order, args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if extra:
+    for extra in phases:
+        if not extra:
+            continue
         for _ in range(args.warmup):
             for name in extra:
                 calls[name]()
