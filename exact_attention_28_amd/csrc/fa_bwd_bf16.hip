@@ -235,9 +235,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     for (int v = 0; v < 16; ++v) dk[mb][v] = dv[mb][v] = 0.f;
 
   // query tiles [32t, 32t + 32) that can see a key of this workgroup,
-  // taken from the last one down, the group's heads inner: every workgroup
-  // of a KV head starts at the same tile and they move through Q and dO
-  // together, so a tile fetched once serves them from L2
+  // taken in order along the query range (direction below), the group's
+  // heads inner: the workgroups of a KV head that run together move
+  // through Q and dO abreast, so a tile fetched once serves them from L2
   const int nqt = (Nq + BR - 1) / BR;
   const int t0 = CAUSAL ? min(nqt, max(0, k0 - off) / BR) : 0;
   const int per_head = nqt - t0;
