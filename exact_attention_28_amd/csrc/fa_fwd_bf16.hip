@@ -291,134 +291,173 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
     return CAUSAL && (tile * kBN > wrow0 + 31 + off);
   };
 
-  // ---- prologue: K(0), V(0), K(1) (and V(1) with three V buffers) in
-  // flight; S(0)
+  // Two passes over the key tiles, of which the second almost never runs.
+  // The exponent reference only keeps P = 2^(S c - m) inside the range of
+  // fp32 and bf16: any reference gives the same softmax. The first pass
+  // fixes it at the row maximum of the first key tile and never moves it,
+  // so a tile needs no row maximum, no reference test and no rescaling of
+  // O (about 30 VALU instructions per tile and wave fewer). A row that
+  // sees anything sees key 0, so every such row has a finite reference
+  // after that tile. Scores that later rise more than ~2^7 above it make
+  // P, l or O overflow; the pass then ends with a non-finite l or O in
+  // some lane, and the workgroup runs the tiles again with the exact lazy
+  // reference of the second pass (moved when a tile's maximum passes it by
+  // kTau, O rescaled then), from a clean state.
   constexpr std::integral_constant<int, 0> B0{};
   constexpr std::integral_constant<int, 1> B1{};
-  if (nt > 0) {
-    issue_k(0, B0);
-    issue_v(0, B0);
-    if (nt > 1) issue_k(1, B1);
-    if (kVStages > 2 && nt > 1) issue_v(1, B1);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x16 sc[2];
-  // row max of the next tile's scores, taken where S is formed (beside the
-  // P.V products of the previous tile); a tile that needs masking takes its
-  // max again after the mask
-  float mx_next = kNegInf;
-  if (nt > 0 && !skip_tile(0)) {
-    qk(B0, sc);
-    mx_next = tile_max<2>(sc);
-  }
-  __syncthreads();  // K buffer 0 is refilled below
+  constexpr std::integral_constant<int, 2> B2{};
+  __shared__ int redo;
+  auto run = [&](auto fixed_ref) {
+    constexpr bool FIXED = decltype(fixed_ref)::value;
+    // ---- prologue: K(0), V(0), K(1) (and V(1) with three V buffers) in
+    // flight; S(0)
+    if (nt > 0) {
+      issue_k(0, B0);
+      issue_v(0, B0);
+      if (nt > 1) issue_k(1, B1);
+      if (kVStages > 2 && nt > 1) issue_v(1, B1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 sc[2];
+    // row max of the next tile's scores, taken where S is formed (beside
+    // the P.V products of the previous tile); a tile that needs masking
+    // takes its max again after the mask
+    float mx_next = kNegInf;
+    if (nt > 0 && !skip_tile(0)) {
+      qk(B0, sc);
+      mx_next = tile_max<2>(sc);
+    }
+    __syncthreads();  // K buffer 0 is refilled below
 
-  // One key tile: S(t) arrives in sc; S(t+1) is computed into sn while P(t)
-  // is formed. Tiles are taken in pairs with the two score buffers swapping
-  // roles, so no tile ends with a register copy.
-  // `par` is t % 2 and `vst` t % kVStages as compile-time indices.
-  auto step = [&](int t, auto par, auto vst, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    constexpr int P = decltype(par)::value;
-    constexpr int VS = decltype(vst)::value;
-    constexpr std::integral_constant<int, P> cur{};
-    constexpr std::integral_constant<int, 1 - P> nxt{};
-    constexpr std::integral_constant<int, VS> vcur{};
-    constexpr std::integral_constant<int, (VS + kVStages - 1) % kVStages> vnew{};
-    const int n0 = t * kBN;
-    // K runs two tiles ahead, V kVStages - 1: both target buffers were last
-    // read before the previous barrier.
-    const bool more_k = t + 2 < nt;
-    const bool more_v = t + kVStages - 1 < nt;
-    if (more_k) issue_k(t + 2, cur);
-    if (more_v) issue_v(t + kVStages - 1, vnew);
-    const bool do_t = !skip_tile(t);
-    if (do_t) {
-      // mask the ragged end of the key range and the causal diagonal
-      const bool need_mask =
-          (n0 + kBN > nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
-      float mx = mx_next;
-      if (need_mask) {
-        const int lim = CAUSAL ? min(nk - 1, row + off) : nk - 1;
+    // One key tile: S(t) arrives in sc; S(t+1) is computed into sn while
+    // P(t) is formed. Tiles are taken in pairs with the two score buffers
+    // swapping roles, so no tile ends with a register copy.
+    // `par` is t % 2 and `vst` t % kVStages as compile-time indices.
+    auto step = [&](int t, auto par, auto vst, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      constexpr int P = decltype(par)::value;
+      constexpr int VS = decltype(vst)::value;
+      constexpr std::integral_constant<int, P> cur{};
+      constexpr std::integral_constant<int, 1 - P> nxt{};
+      constexpr std::integral_constant<int, VS> vcur{};
+      constexpr std::integral_constant<int, (VS + kVStages - 1) % kVStages> vnew{};
+      const int n0 = t * kBN;
+      // K runs two tiles ahead, V kVStages - 1: both target buffers were
+      // last read before the previous barrier.
+      const bool more_k = t + 2 < nt;
+      const bool more_v = t + kVStages - 1 < nt;
+      if (more_k) issue_k(t + 2, cur);
+      if (more_v) issue_v(t + kVStages - 1, vnew);
+      const bool do_t = !skip_tile(t);
+      if (do_t) {
+        // mask the ragged end of the key range and the causal diagonal
+        const bool need_mask =
+            (n0 + kBN > nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
+        if (need_mask) {
+          const int lim = CAUSAL ? min(nk - 1, row + off) : nk - 1;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int key = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
+              if (key > lim) sc[kb][v] = kNegInf;
+            }
+        }
+        if (!FIXED || t == 0) {
+          const float mx = need_mask ? tile_max<2>(sc) : mx_next;
+          const float alpha = move_reference(mx, st, c);
+          // rescale O before the MFMA work below, so that the S(t+1)
+          // product and the P(t) arithmetic share one branch-free block
+          if (!FIXED && __any(alpha != 1.f)) {
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) o[mb][v] *= alpha;
+          }
+        }
+        uint32_t pw[2][2][4];
+        // S(t+1) on the matrix cores while P(t) is formed on the VALU. Run
+        // without a branch (so both sit in one basic block and
+        // interleave): past the last tile, or beyond this wave's causal
+        // rows, the result is never read, and the K buffer it reads is not
+        // being written.
+        // raised issue priority while this wave feeds the matrix cores:
+        // the other wave on the SIMD (a wave of this workgroup: the 83 KB
+        // of LDS leave room for one workgroup per CU) fills in with its
+        // VALU work
+        __builtin_amdgcn_s_setprio(1);
+        qk(nxt, sn);
+        softmax_exp_pack<2>(sc, st, c, pw);
+        // O^T += V^T P^T, 16 keys per MFMA: lane half h contracts keys
+        // 32kb + 16j + 4h + {0..3} (items 0..3) and +8 (items 4..7)
+        const lds_char* vp0 = vbuf(vcur) + vfrag;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (key > lim) sc[kb][v] = kNegInf;
+          for (int j = 0; j < 2; ++j) {
+            u32x4 pv = {pw[kb][j][0], pw[kb][j][1], pw[kb][j][2], pw[kb][j][3]};
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
+            const int rb = 32 * kb + 16 * j;              // multiple of 16
+            const int vimm = (rb / (4 * T::RPB)) * T::VPITCH +
+                             ((rb / 4) % T::RPB) * (2 * D);
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb) {
+              const lds_char* vp = vp0 + vimm + 64 * mb;
+              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                  (__attribute__((address_space(3))) bf16x4*)(vp));
+              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                  (__attribute__((address_space(3))) bf16x4*)(vp + 2 * (2 * D)));
+              const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              o[mb] = mfma_32x32x16_bf16(a, pb, o[mb]);
+            }
           }
-        mx = tile_max<2>(sc);
+        if (!FIXED) mx_next = tile_max<2>(sn);
+        __builtin_amdgcn_s_setprio(0);
       }
-      const float alpha = move_reference(mx, st, c);
-      // rescale O before the MFMA work below, so that the S(t+1) product
-      // and the P(t) arithmetic share one branch-free block
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[mb][v] *= alpha;
+      // tile t+1 needs K(t+2) and V(t+1), so only the V(t+2) loads just
+      // issued (the last BPW in flight) could stay pending; the barrier's
+      // workgroup fence then waits for the wave's remaining direct loads
+      // as well, so every load has this tile's compute time to land
+      if (kVStages > 2 && more_v) __builtin_amdgcn_s_waitcnt(0x0F70 | T::BPW);
+      else wait_vm0();
+      __syncthreads();
+    };
+    f32x16 sb[2];
+    if constexpr (kVStages == 2) {
+      for (int t = 0; t < nt; t += 2) {
+        step(t, B0, B0, sc, sb);
+        if (t + 1 < nt) step(t + 1, B1, B1, sb, sc);
       }
-      uint32_t pw[2][2][4];
-      // S(t+1) on the matrix cores while P(t) is formed on the VALU. Run
-      // without a branch (so both sit in one basic block and interleave):
-      // past the last tile, or beyond this wave's causal rows, the result is
-      // never read, and the K buffer it reads is not being written.
-      // raised issue priority while this wave feeds the matrix cores: the
-      // other wave on the SIMD (a wave of this workgroup: the 83 KB of LDS
-      // leave room for one workgroup per CU) fills in with its VALU work
-      __builtin_amdgcn_s_setprio(1);
-      qk(nxt, sn);
-      softmax_exp_pack<2>(sc, st, c, pw);
-      // O^T += V^T P^T, 16 keys per MFMA: lane half h contracts keys
-      // 32kb + 16j + 4h + {0..3} (items 0..3) and +8 (items 4..7)
-      const lds_char* vp0 = vbuf(vcur) + vfrag;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4 pv = {pw[kb][j][0], pw[kb][j][1], pw[kb][j][2], pw[kb][j][3]};
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
-          const int rb = 32 * kb + 16 * j;              // multiple of 16
-          const int vimm = (rb / (4 * T::RPB)) * T::VPITCH +
-                           ((rb / 4) % T::RPB) * (2 * D);
-#pragma unroll
-          for (int mb = 0; mb < D / 32; ++mb) {
-            const lds_char* vp = vp0 + vimm + 64 * mb;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4*)(vp));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4*)(vp + 2 * (2 * D)));
-            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            o[mb] = mfma_32x32x16_bf16(a, pb, o[mb]);
-          }
-        }
-      mx_next = tile_max<2>(sn);
-      __builtin_amdgcn_s_setprio(0);
+    } else {
+      for (int t = 0; t < nt; t += 6) {
+        step(t, B0, B0, sc, sb);
+        if (t + 1 < nt) step(t + 1, B1, B1, sb, sc);
+        if (t + 2 < nt) step(t + 2, B0, B2, sc, sb);
+        if (t + 3 < nt) step(t + 3, B1, B0, sb, sc);
+        if (t + 4 < nt) step(t + 4, B0, B1, sc, sb);
+        if (t + 5 < nt) step(t + 5, B1, B2, sb, sc);
+      }
     }
-    // tile t+1 needs K(t+2) and V(t+1), so only the V(t+2) loads just
-    // issued (the last BPW in flight) could stay pending; the barrier's
-    // workgroup fence then waits for the wave's remaining direct loads as
-    // well, so every load has this tile's compute time to land
-    if (kVStages > 2 && more_v) __builtin_amdgcn_s_waitcnt(0x0F70 | T::BPW);
-    else wait_vm0();
-    __syncthreads();
   };
-  f32x16 sb[2];
-  constexpr std::integral_constant<int, 2> B2{};
-  if constexpr (kVStages == 2) {
-    for (int t = 0; t < nt; t += 2) {
-      step(t, B0, B0, sc, sb);
-      if (t + 1 < nt) step(t + 1, B1, B1, sb, sc);
-    }
-  } else {
-    for (int t = 0; t < nt; t += 6) {
-      step(t, B0, B0, sc, sb);
-      if (t + 1 < nt) step(t + 1, B1, B1, sb, sc);
-      if (t + 2 < nt) step(t + 2, B0, B2, sc, sb);
-      if (t + 3 < nt) step(t + 3, B1, B0, sb, sc);
-      if (t + 4 < nt) step(t + 4, B0, B1, sc, sb);
-      if (t + 5 < nt) step(t + 5, B1, B2, sb, sc);
-    }
+  if (tid == 0) redo = 0;
+  run(std::true_type{});
+  {
+    // inf or NaN anywhere in this lane's l, lr or O shows up in the sum
+    float chk = st.l + st.lr;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) chk += o[mb][v] * 0.f;
+    if (__any(!__builtin_isfinite(chk)) && lane == 0) redo = 1;
+  }
+  __syncthreads();
+  if (redo) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
+    st = RowState{kNegInf, 0.f, 0.f};
+    run(std::false_type{});
   }
 
   // ---- epilogue: O = O^T / lr, LSE = ln 2 * (m + log2 l)
