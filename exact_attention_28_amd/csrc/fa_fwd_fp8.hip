@@ -223,107 +223,142 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     return CAUSAL && (tile * kBN > wrow0 + 31 + off);
   };
 
-  // ---- prologue: K(0), V(0), K(1) in flight; S(0)
+  // Two passes, the second almost never run (as in the bf16 kernel): the
+  // first fixes the exponent reference at the first key tile's row
+  // maximum and never moves it, so a tile needs no row maximum, reference
+  // test or O rescale. P then stays at most 2^(later max - first max);
+  // once that passes the e4m3 range, its conversion gives NaN codes (no
+  // saturation), which reach O and the rounded sum; the workgroup then
+  // runs its tiles again with the lazy reference (P <= 2^8 = 256 < 448).
   constexpr std::integral_constant<int, 0> B0{};
   constexpr std::integral_constant<int, 1> B1{};
-  if (nt > 0) {
-    issue_k(0, B0);
-    issue_v(0, B0);
-    if (nt > 1) issue_k(1, B1);
-  }
-  wait_vm0();
-  __syncthreads();
-  f32x16 sc[2];
-  // row max of the next tile's scores, taken beside the previous tile's P.V
-  // products; a tile that needs masking takes its max again after the mask
-  float mx_next = kNegInf;
-  if (nt > 0 && !skip_tile(0)) {
-    qk(B0, sc);
-    mx_next = tile_max<2>(sc);
-  }
-  __syncthreads();  // K buffer 0 is refilled below
-
-  // One key tile t (parity P): S(t) arrives in sc, S(t+1) is computed into
-  // sn while P(t) is formed. K runs two tiles ahead and V one: both target
-  // buffers were last read before the previous barrier. Tiles are taken in
-  // pairs with the score buffers swapping roles (no register copies).
-  auto step = [&](int t, auto par, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    constexpr int P = decltype(par)::value;
-    constexpr std::integral_constant<int, P> cur{};
-    constexpr std::integral_constant<int, 1 - P> nxt{};
-    const int n0 = t * kBN;
-    if (t + 2 < nt) issue_k(t + 2, cur);
-    if (t + 1 < nt) issue_v(t + 1, nxt);
-    if (!skip_tile(t)) {
-      const bool need_mask =
-          (n0 + kBN > Nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
-      float mx = mx_next;
-      if (need_mask) {
-        const int lim = CAUSAL ? min(Nk - 1, row + off) : Nk - 1;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (key > lim) sc[kb][v] = kNegInf;
-          }
-        mx = tile_max<2>(sc);
-      }
-      const float alpha = move_reference(mx, st, c);
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[mb][v] *= alpha;
-        lsum[0] *= alpha;
-      }
-      // S(t+1) on the matrix cores while P(t) is formed on the VALU (past
-      // the last tile, or beyond this wave's causal rows, the product is
-      // never read and its buffer is not being written)
-      // raised issue priority while this wave feeds the matrix cores: the
-      // other wave of the SIMD fills in with its VALU work
-      __builtin_amdgcn_s_setprio(1);
-      qk(nxt, sn);
-      const float mref = (st.m == kNegInf) ? 0.f : st.m;
-      float sum = 0.f;
-      i32x8 pb;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int kb = jj >> 2, v0 = 4 * (jj & 3);
-        float p4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p4[e] = fast_exp2(__builtin_fmaf(sc[kb][v0 + e], c, -mref));
-          sum += p4[e];
-        }
-        pb[jj] = (int)pack_e4m3x4(p4[0], p4[1], p4[2], p4[3]);
-      }
-      st.l += sum;
-      lsum = mfma_32x32x64_fp4_e4m3(ones, pb, lsum);
-      const lds_char* vp = vbuf(cur);
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) {
-        i32x8 a;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          typedef int v2i __attribute__((ext_vector_type(2)));
-          const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) v2i*)(vp + vaddr[j] + 32 * mb));
-          a[2 * j] = r[0];
-          a[2 * j + 1] = r[1];
-        }
-        o[mb] = mfma_32x32x64_e4m3(a, pb, o[mb]);
-      }
-      mx_next = tile_max<2>(sn);
-      __builtin_amdgcn_s_setprio(0);
+  __shared__ int redo;
+  auto run = [&](auto fixed_ref) {
+    constexpr bool FIXED = decltype(fixed_ref)::value;
+    // ---- prologue: K(0), V(0), K(1) in flight; S(0)
+    if (nt > 0) {
+      issue_k(0, B0);
+      issue_v(0, B0);
+      if (nt > 1) issue_k(1, B1);
     }
     wait_vm0();
     __syncthreads();
+    f32x16 sc[2];
+    // row max of the next tile's scores, taken beside the previous tile's P.V
+    // products; a tile that needs masking takes its max again after the mask
+    float mx_next = kNegInf;
+    if (nt > 0 && !skip_tile(0)) {
+      qk(B0, sc);
+      mx_next = tile_max<2>(sc);
+    }
+    __syncthreads();  // K buffer 0 is refilled below
+
+    // One key tile t (parity P): S(t) arrives in sc, S(t+1) is computed into
+    // sn while P(t) is formed. K runs two tiles ahead and V one: both target
+    // buffers were last read before the previous barrier. Tiles are taken in
+    // pairs with the score buffers swapping roles (no register copies).
+    auto step = [&](int t, auto par, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      constexpr int P = decltype(par)::value;
+      constexpr std::integral_constant<int, P> cur{};
+      constexpr std::integral_constant<int, 1 - P> nxt{};
+      const int n0 = t * kBN;
+      if (t + 2 < nt) issue_k(t + 2, cur);
+      if (t + 1 < nt) issue_v(t + 1, nxt);
+      if (!skip_tile(t)) {
+        const bool need_mask =
+            (n0 + kBN > Nk) || (CAUSAL && n0 + kBN - 1 > wrow0 + off);
+        if (need_mask) {
+          const int lim = CAUSAL ? min(Nk - 1, row + off) : Nk - 1;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int key = n0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
+              if (key > lim) sc[kb][v] = kNegInf;
+            }
+        }
+        if (!FIXED || t == 0) {
+          const float mx = need_mask ? tile_max<2>(sc) : mx_next;
+          const float alpha = move_reference(mx, st, c);
+          if (!FIXED && __any(alpha != 1.f)) {
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) o[mb][v] *= alpha;
+            lsum[0] *= alpha;
+          }
+        }
+        // S(t+1) on the matrix cores while P(t) is formed on the VALU (past
+        // the last tile, or beyond this wave's causal rows, the product is
+        // never read and its buffer is not being written)
+        // raised issue priority while this wave feeds the matrix cores: the
+        // other wave of the SIMD fills in with its VALU work
+        __builtin_amdgcn_s_setprio(1);
+        qk(nxt, sn);
+        const float mref = (st.m == kNegInf) ? 0.f : st.m;
+        float sum = 0.f;
+        i32x8 pb;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int kb = jj >> 2, v0 = 4 * (jj & 3);
+          float p4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p4[e] = fast_exp2(__builtin_fmaf(sc[kb][v0 + e], c, -mref));
+            sum += p4[e];
+          }
+          pb[jj] = (int)pack_e4m3x4(p4[0], p4[1], p4[2], p4[3]);
+        }
+        st.l += sum;
+        lsum = mfma_32x32x64_fp4_e4m3(ones, pb, lsum);
+        const lds_char* vp = vbuf(cur);
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) {
+          i32x8 a;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            typedef int v2i __attribute__((ext_vector_type(2)));
+            const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i*)(vp + vaddr[j] + 32 * mb));
+            a[2 * j] = r[0];
+            a[2 * j + 1] = r[1];
+          }
+          o[mb] = mfma_32x32x64_e4m3(a, pb, o[mb]);
+        }
+        if (!FIXED) mx_next = tile_max<2>(sn);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      wait_vm0();
+      __syncthreads();
+    };
+    f32x16 sb[2];
+    for (int t = 0; t < nt; t += 2) {
+      step(t, B0, sc, sb);
+      if (t + 1 < nt) step(t + 1, B1, sb, sc);
+    }
+
   };
-  f32x16 sb[2];
-  for (int t = 0; t < nt; t += 2) {
-    step(t, B0, sc, sb);
-    if (t + 1 < nt) step(t + 1, B1, sb, sc);
+  if (tid == 0) redo = 0;
+  run(std::true_type{});
+  {
+    // inf or NaN anywhere in this lane's l, rounded sum or O
+    float chk = st.l + lsum[0];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) chk += o[mb][v] * 0.f;
+    if (__any(!__builtin_isfinite(chk)) && lane == 0) redo = 1;
+  }
+  __syncthreads();
+  if (redo) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[mb][v] = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) lsum[v] = 0.f;
+    st = RowState{kNegInf, 0.f, 0.f};
+    run(std::false_type{});
   }
 
   // ---- epilogue: O = s_v * O^T / lr, LSE = ln 2 * (m + log2 l)

@@ -122,30 +122,37 @@ def test_fwd_rising_scores_rescale_path(fa, dtype):
              f"rising {dtype}")
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_fwd_scores_far_above_the_first_tile(fa, causal):
-    """The first 64 keys score about 2^300 below the rest (in the exponent
-    base 2 the kernel works in): a reference fixed at the first key tile
-    would overflow P, so the kernel must finish these rows with its moving
-    reference, and still match the definition."""
+@pytest.mark.parametrize("dtype,causal", [("bf16", False), ("bf16", True),
+                                          ("fp8", False), ("fp8", True)])
+def test_fwd_scores_far_above_the_first_tile(fa, dtype, causal):
+    """The first 64 keys score about 2^270 below the rest (in the exponent
+    base 2 the kernels work in): a reference fixed at the first key tile
+    would overflow P (bf16: past fp32; e4m3: past 448), so the kernel must
+    finish these rows with its moving reference, and still match the
+    definition."""
     B, H, N, d = 1, 2, 300 if causal else 700, 128
     rng = np.random.default_rng(11)
     q = (np.abs(rng.standard_normal((B, H, N, d))) + 1.0).astype(np.float32)
     k = rng.standard_normal((B, H, N, d)).astype(np.float32)
     v = rng.standard_normal((B, H, N, d)).astype(np.float32)
     k[:, :, :64] -= 10.0
-    inp = W.PrefillInputs(*[W._to_storage(x, "bf16")[0] for x in (q, k, v)],
+    inp = W.PrefillInputs(*[W._to_storage(x, dtype)[0] for x in (q, k, v)],
                           scale=1.0 / math.sqrt(d), causal=causal,
-                          dtype="bf16", descale=None)
+                          dtype=dtype, descale=None)
+    if dtype == "fp8":
+        inp.descale = tuple(W._to_storage(x, "fp8")[1] for x in (q, k, v))
     # the gap the inputs really have, in log2 units of the scaled scores:
     # key 64 (which every row from 64 on sees) against the first tile
     qs, ks = W.as_f64(inp.q)[0, 0], W.as_f64(inp.k)[0, 0]
+    if dtype == "fp8":
+        qs, ks = qs * inp.descale[0], ks * inp.descale[1]
     s2 = (qs @ ks.T) * inp.scale / math.log(2.0)
     gap = s2[64:, 64] - np.max(s2[64:, :64], axis=1)
     assert np.min(gap) > 200
     o, lse = _gpu_fwd(fa, inp)
     ro, rl = _oracle_fwd(inp)
-    _compare(o, lse, ro, rl, "bf16", f"far above the first tile causal={causal}")
+    _compare(o, lse, ro, rl, dtype,
+             f"far above the first tile {dtype} causal={causal}")
 
 
 def test_fwd_fully_masked_rows(fa):
