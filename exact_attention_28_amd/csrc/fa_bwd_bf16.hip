@@ -44,28 +44,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 
-// Direct global->LDS loads (16 or 4 bytes per lane) written out as
-// instructions. The loops below read LDS while their next tile's direct
-// loads are in flight; a direct load issued through the compiler's builtin
-// counts there as an LDS access of unknown order, and the compiler then
-// waits for every outstanding LDS read (lgkmcnt 0) wherever it needs one,
-// so no fragment read can run ahead of the products that use it. Issued
-// this way the loads are invisible to its wait counting: the kernels wait
-// for them themselves (wait_vm0 before the barrier that publishes a tile),
-// and the waits the compiler computes for its own loads can only become
-// more conservative. M0 carries the wave's LDS base; the s_nop is the one
-// wait state a direct load needs after M0 is written.
-__device__ __forceinline__ void g2lds_16B_own(const void* g, lds_char* l) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0)
-               : "memory");
-}
-__device__ __forceinline__ void g2lds_4B_own(const void* g, lds_char* l) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0)
-               : "memory");
-}
-
 // A row-major tile of ROWS rows x D bf16 in LDS, as 1 KB blocks (one direct
 // load instruction: 64 lanes x 16 B) at a pitch of 1 KB + 16 B. RowTile
 // below and IlvTile (the interleaved layout, fa_device.h) share one

@@ -53,6 +53,28 @@ __device__ __forceinline__ void g2lds_16B(const void* g, lds_char* l) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l,
                                    16, 0, 0);
 }
+// The same direct loads (16 or 4 bytes per lane) written out as
+// instructions, for loops that read LDS while their next tiles' direct
+// loads are in flight: a direct load issued through the compiler's builtin
+// counts there as an LDS access of unknown order, and the compiler then
+// waits for every outstanding LDS read (lgkmcnt 0) wherever it needs one,
+// so no fragment read can run ahead of the products that use it. Issued
+// this way the loads are invisible to its wait counting: a kernel using
+// them waits for them itself (a vmcnt wait before the barrier that
+// publishes a tile), and the waits the compiler computes for its own loads
+// can only become more conservative. M0 carries the wave's LDS base; the s_nop is the one
+// wait state a direct load needs after M0 is written.
+__device__ __forceinline__ void g2lds_16B_own(const void* g, lds_char* l) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0)
+               : "memory");
+}
+__device__ __forceinline__ void g2lds_4B_own(const void* g, lds_char* l) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0)
+               : "memory");
+}
+
 // s_waitcnt vmcnt(0): the direct loads of this wave have reached LDS.
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -232,16 +232,16 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
     if (PAGED && n0 + kBN <= nk) {
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(Kh + page_off(n0, kpg[i]) + kpo[i], dst + kWaves * i * T::KPITCH);
+        g2lds_16B_own(Kh + page_off(n0, kpg[i]) + kpo[i], dst + kWaves * i * T::KPITCH);
     } else if (!PAGED && n0 + kBN <= nk) {
       const __bf16* src = Kh + (long)n0 * D;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(src + koff[i], dst + kWaves * i * T::KPITCH);
+        g2lds_16B_own(src + koff[i], dst + kWaves * i * T::KPITCH);
     } else {
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(Kh + row_elem(n0, k_row(w + kWaves * i)) + 8 * chunk,
+        g2lds_16B_own(Kh + row_elem(n0, k_row(w + kWaves * i)) + 8 * chunk,
                   dst + kWaves * i * T::KPITCH);
     }
   };
@@ -251,16 +251,16 @@ __global__ __launch_bounds__(kThreads, 512 / kThreads) void fwd_bf16_kernel(
     if (PAGED && n0 + kBN <= nk) {
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(Vh + page_off(n0, vpg[i]) + vpo[i], dst + kWaves * i * T::VPITCH);
+        g2lds_16B_own(Vh + page_off(n0, vpg[i]) + vpo[i], dst + kWaves * i * T::VPITCH);
     } else if (!PAGED && n0 + kBN <= nk) {
       const __bf16* src = Vh + (long)n0 * D;
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(src + voff[i], dst + kWaves * i * T::VPITCH);
+        g2lds_16B_own(src + voff[i], dst + kWaves * i * T::VPITCH);
     } else {
 #pragma unroll
       for (int i = 0; i < T::BPW; ++i)
-        g2lds_16B(Vh + row_elem(n0, v_row(w + kWaves * i)) + 8 * chunk,
+        g2lds_16B_own(Vh + row_elem(n0, v_row(w + kWaves * i)) + 8 * chunk,
                   dst + kWaves * i * T::VPITCH);
     }
   };

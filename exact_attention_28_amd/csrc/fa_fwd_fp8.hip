@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const int last = min(kBN, Nk - n0) - 1;
 #pragma unroll
     for (int i = 0; i < T::BPW; ++i)
-      g2lds_16B(src + (long)min(k_row(w + 4 * i), last) * D,
+      g2lds_16B_own(src + (long)min(k_row(w + 4 * i), last) * D,
                 dst + 4 * i * T::PITCH);
   };
   // V: the piece this lane moves (see the layout above)
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const int last = min(kBN, Nk - n0) - 1;
 #pragma unroll
     for (int i = 0; i < T::BPW; ++i)
-      g2lds_16B(src + (long)min(v_row<D>(w + 4 * i, vslot), last) * D,
+      g2lds_16B_own(src + (long)min(v_row<D>(w + 4 * i, vslot), last) * D,
                 dst + 4 * i * T::PITCH);
   };
 
