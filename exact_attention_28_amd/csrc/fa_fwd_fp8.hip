@@ -6,9 +6,12 @@
 // the listing's fp16). Inputs carry per-tensor fp32 scales s_q, s_k, s_v:
 // s_q*s_k is folded with scale*log2(e) into the single multiply that turns
 // raw scores into exp2 arguments, and s_v into the final 1/l.
-// P is the unnormalised exp2(s - m_ref) <= 2^kTau = 256 < 448, so it fits
-// e4m3 without a scale. O is normalised by the sum of the rounded P (an
-// exact convex combination of V rows), LSE uses the sum of the fp32 P.
+// P is the unnormalised exp2(s - m_ref), rounded to e4m3 without a scale:
+// with the first pass's fixed reference it stays below 448 unless later
+// scores rise about 2^9 above the first key tile (then its conversion gives
+// NaN and the lazy second pass, P <= 2^kTau = 256, takes over). O is
+// normalised by the sum of the rounded P (an exact convex combination of V
+// rows), LSE uses the sum of the fp32 P.
 //
 // Structure as the bf16 kernel: one workgroup (4 waves, 32 rows each) per
 // 128-row query tile, 64-key K/V tiles arriving by direct global->LDS loads
