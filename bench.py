@@ -34,6 +34,14 @@ cpu_baseline: the fp64 oracle on this host, before the GPU is touched: a
 pool of one worker per core (at most 16) with one BLAS thread each, over
 256-row blocks of the causal prefill (about 12 s of work) and every request
 of the paged decode; core count and CPU model are stated.
+
+--sweep (not part of the default run) measures instead the sequence sweep
+of the capstone page's roofline lab (h = 32, d = 128, non-causal, N = 1K to
+32K): the fused forward against the three-kernel contrast that writes S
+and P to HBM, beside the page's roofline model of the two (traffic 8Nd +
+8N^2 bytes per head for the contrast as its §1.1 derives, 8Nd for the
+fused pass; FLOPs 4N^2 d + 3N^2) at this GPU's peaks, and prints one JSON
+line with a row per N.
 """
 from __future__ import annotations
 
@@ -323,6 +331,106 @@ def cpu_baseline(prefill_inp, decode_inp, target_s=12.0, rows=256):
     return out
 
 
+def sweep(steps, warmup):
+    """The capstone roofline lab's sweep (h = 32, d = 128, N = 1K..32K,
+    non-causal, one sequence) measured: fused forward and the three-kernel
+    contrast, HIP events around each launch, median of `steps`; the lab's
+    traffic model at MI355X peaks beside each row. Inputs: seeded N(0,1)
+    draws rounded to bf16 (the workloads module, seed 42)."""
+    import torch
+    import workloads as W
+    import exact_attention_28_amd as fa
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    H, d = 32, 128
+    rows = []
+    for n in (1024, 2048, 4096, 8192, 16384, 32768):
+        inp = W.prefill_inputs(1, H, H, n, n, d, dtype="bf16", causal=False,
+                               seed=42)
+        q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+        del inp
+        of = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        on = torch.empty_like(of)
+        lf = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        ln = torch.empty_like(lf)
+        # the contrast's softmax holds a row in one workgroup: rows of at
+        # most 16384 scores (the entry point refuses longer ones)
+        with_naive = n <= 16384
+        ws = torch.empty(fa.fa_naive_workspace_size(1, H, n, n) if with_naive
+                         else 256, dtype=torch.uint8, device=dev)
+        args_ = (1, H, H, n, n, d, d ** -0.5, False)
+        calls = {"fused": lambda: fa.fa_fwd(q, k, v, of, lf, *args_,
+                                            fa.FA_DTYPE_BF16, None, stream)}
+        if with_naive:
+            calls["naive"] = lambda: fa.fa_naive_attention(
+                q, k, v, on, ln, *args_, ws, ws.numel(), stream)
+        ms = {}
+        for name, call in calls.items():
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            ev = []
+            for _ in range(steps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call()
+                e1.record(stream)
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            ms[name] = statistics.median(a.elapsed_time(b) for a, b in ev)
+        diff = (float((of.float() - on.float()).abs().max()) if with_naive
+                else None)
+        del ws
+        flops = 4.0 * n * n * d * H           # the two products
+        flops_sm = 3.0 * n * n * H            # the softmax (reported apart)
+        # the page's ledger (§1.1): Q, K, V, O once (8Nd bytes) and S, P
+        # written and read once each at 2 bytes an element (8N^2 bytes)
+        b_naive = H * (8 * n * d + 8 * n * n)
+        b_fused = H * (8 * n * d)
+        t_c = (flops + flops_sm) / (PEAK_BF16_TFLOPS * 1e12)
+        model = max(t_c, b_naive / (PEAK_HBM_GBS * 1e9)) / max(
+            t_c, b_fused / (PEAK_HBM_GBS * 1e9))
+        # the same model as the page's lab script evaluates it: its A100
+        # figures (312 TFLOPS, 2039 GB/s) and its byte count, which doubles
+        # the §1.1 ledger
+        t_ca = (flops + flops_sm) / 312e12
+        model_lab = max(t_ca, 2 * b_naive / 2039e9) / max(t_ca,
+                                                          b_fused / 2039e9)
+        tn = ms.get("naive")
+        rows.append({
+            "N": n, "fused_ms": ms["fused"], "naive_ms": tn,
+            "fused_tflops": flops / (ms["fused"] * 1e-3) / 1e12,
+            "fused_frac_bf16_peak": flops / (ms["fused"] * 1e-3) / 1e12 /
+            PEAK_BF16_TFLOPS,
+            "naive_tflops": flops / (tn * 1e-3) / 1e12 if tn else None,
+            "naive_ledger_bytes": b_naive,
+            "naive_ledger_GB/s": b_naive / (tn * 1e-3) / 1e9 if tn else None,
+            "fused_ledger_bytes": b_fused,
+            "speedup_measured": tn / ms["fused"] if tn else None,
+            "speedup_model_mi355x": model,
+            "speedup_model_lab_a100": model_lab,
+            "max_abs_fused_minus_naive": diff,
+        })
+        print(f"bench sweep: N={n} fused {ms['fused']:.3f} ms"
+              + (f", naive {tn:.3f} ms ({tn / ms['fused']:.2f}x, model "
+                 f"{model:.2f}x), |fused - naive| <= {diff:.2e}" if tn else
+                 f" (model speedup {model:.2f}x; no contrast past 16384)"),
+              file=sys.stderr, flush=True)
+        del q, k, v, of, on, lf, ln
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": "fused vs three-kernel attention forward over sequence "
+                  "length (capstone roofline lab sweep)",
+        "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "B=1 H=32 d=128 non-causal N=1K..32K",
+                   "seed": 42},
+        "sweep": rows}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,12 +445,18 @@ def main():
                     default="prefill,decode,fp8,bwd,decode8,noncausal,naive,"
                     "chunked",
                     help="comma list of legs to run (profiling runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the sequence sweep of the capstone roofline "
+                    "lab: fused vs three-kernel forward, N = 1K..32K")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only (asked for --gpus "
               f"{args.gpus}); multi-GPU sharding is not implemented",
               file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(args.steps, args.warmup)
+        return
 
     import torch
     import workloads as W

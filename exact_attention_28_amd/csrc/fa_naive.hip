@@ -140,12 +140,14 @@ __global__ __launch_bounds__(kThreads, 2) void naive_scores_kernel(
 }
 
 // -------------------------------------------------------- P = softmax(S)
-// One workgroup per row: the row's scores are read once into registers
-// (NV per thread), the three passes of the safe softmax ([Capstone §2.1])
-// run on them with workgroup reductions, and P (bf16) is written over the
-// row, with the row's LSE. Bottom-right causal mask: key j visible to row
-// i iff j <= i + Nk - Nq.
-template <int NV>
+// One workgroup per row (rows of more than 4096 keys): the row's scores
+// are read once into registers as 16-byte pieces of 8 (Nk is a multiple of
+// 8, so rows are 16-byte aligned; NP pieces per thread), the three passes
+// of the safe softmax ([Capstone §2.1]) run on them with workgroup
+// reductions, and P (bf16) is written over the row as 16-byte pieces, with
+// the row's LSE. Bottom-right causal mask: key j visible to row i iff
+// j <= i + Nk - Nq.
+template <int NP>  // 8-score pieces per thread: NP * 8 * kThreads >= Nk
 __global__ __launch_bounds__(kThreads) void naive_softmax_kernel(
     _Float16* __restrict__ S, float* __restrict__ LSE, int Nq, int Nk,
     bool causal) {
@@ -155,11 +157,14 @@ __global__ __launch_bounds__(kThreads) void naive_softmax_kernel(
   const int lim = causal ? min(Nk, i + (Nk - Nq) + 1) : Nk;  // visible keys
   _Float16* srow = S + rowid * Nk;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float x[NV];
+  float x[NP][8];
 #pragma unroll
-  for (int e = 0; e < NV; ++e) {
-    const int j = tid + kThreads * e;
-    x[e] = (j < lim) ? (float)srow[j] : kNegInf;
+  for (int c = 0; c < NP; ++c) {
+    const int j0 = 8 * (tid + kThreads * c);
+    f16x8 v8 = {};
+    if (j0 < Nk) v8 = *reinterpret_cast<const f16x8*>(srow + j0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[c][e] = (j0 + e < lim) ? (float)v8[e] : kNegInf;
   }
   auto block_reduce = [&](float v, bool is_max) {
 #pragma unroll
@@ -177,22 +182,31 @@ __global__ __launch_bounds__(kThreads) void naive_softmax_kernel(
   };
   float m = kNegInf;
 #pragma unroll
-  for (int e = 0; e < NV; ++e) m = fmaxf(m, x[e]);
+  for (int c = 0; c < NP; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, x[c][e]);
   m = block_reduce(m, true);
   const float mref = (m == kNegInf) ? 0.f : m;
   float l = 0.f;
 #pragma unroll
-  for (int e = 0; e < NV; ++e) {
-    x[e] = fast_exp2((x[e] - mref) * kLog2e);
-    l += x[e];
-  }
+  for (int c = 0; c < NP; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[c][e] = fast_exp2((x[c][e] - mref) * kLog2e);
+      l += x[c][e];
+    }
   l = block_reduce(l, false);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   __bf16* prow = reinterpret_cast<__bf16*>(srow);
 #pragma unroll
-  for (int e = 0; e < NV; ++e) {
-    const int j = tid + kThreads * e;
-    if (j < Nk) prow[j] = (__bf16)(x[e] * inv);
+  for (int c = 0; c < NP; ++c) {
+    const int j0 = 8 * (tid + kThreads * c);
+    if (j0 < Nk) {
+      bf16x8 p8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p8[e] = (__bf16)(x[c][e] * inv);
+      *reinterpret_cast<bf16x8*>(prow + j0) = p8;
+    }
   }
   if (tid == 0 && LSE != nullptr) LSE[rowid] = l > 0.f ? m + __logf(l) : kNegInf;
 }
@@ -365,7 +379,7 @@ hipError_t launch(const NaiveArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned rows = (unsigned)((long)a.B * a.Hq * a.Nq);
-  const int nv = (a.Nk + kThreads - 1) / kThreads;
+  const int np = (a.Nk + 8 * kThreads - 1) / (8 * kThreads);  // <= 8: Nk <= 16384
   const int nc = (a.Nk + 511) / 512;
   const unsigned wgrid = (rows + kThreads / 64 - 1) / (kThreads / 64);
   if (nc <= 1)
@@ -380,17 +394,11 @@ hipError_t launch(const NaiveArgs& a) {
   else if (nc <= 8)
     hipLaunchKernelGGL((naive_softmax_wave_kernel<8>), dim3(wgrid), dim3(kThreads), 0,
                        a.stream, S, a.lse, (long)rows, a.Nq, a.Nk, a.causal);
-  else if (nv <= 8)
-    hipLaunchKernelGGL((naive_softmax_kernel<8>), dim3(rows), dim3(kThreads), 0,
-                       a.stream, S, a.lse, a.Nq, a.Nk, a.causal);
-  else if (nv <= 16)
-    hipLaunchKernelGGL((naive_softmax_kernel<16>), dim3(rows), dim3(kThreads), 0,
-                       a.stream, S, a.lse, a.Nq, a.Nk, a.causal);
-  else if (nv <= 32)
-    hipLaunchKernelGGL((naive_softmax_kernel<32>), dim3(rows), dim3(kThreads), 0,
+  else if (np <= 4)
+    hipLaunchKernelGGL((naive_softmax_kernel<4>), dim3(rows), dim3(kThreads), 0,
                        a.stream, S, a.lse, a.Nq, a.Nk, a.causal);
   else
-    hipLaunchKernelGGL((naive_softmax_kernel<64>), dim3(rows), dim3(kThreads), 0,
+    hipLaunchKernelGGL((naive_softmax_kernel<8>), dim3(rows), dim3(kThreads), 0,
                        a.stream, S, a.lse, a.Nq, a.Nk, a.causal);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -495,6 +495,8 @@ def _gpu_naive(fa, inp):
                                         # the last lanes' pieces past Nk
     (1, 2, 2, 64, 2048, 128, True),     # the benchmark's row length
     (1, 2, 2, 40, 4104, 64, True),      # past one wave per row
+    (1, 2, 1, 24, 6000, 128, False),    # a workgroup per row, 3 pieces a thread
+    (1, 1, 1, 16, 16384, 64, True),     # the longest row the contrast takes
 ])
 def test_naive_matches_oracle(fa, B, Hq, Hkv, Nq, Nk, d, causal):
     inp = W.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", causal=causal,
