@@ -40,8 +40,10 @@ of the capstone page's roofline lab (h = 32, d = 128, non-causal, N = 1K to
 32K): the fused forward against the three-kernel contrast that writes S
 and P to HBM, beside the page's roofline model of the two (traffic 8Nd +
 8N^2 bytes per head for the contrast as its §1.1 derives, 8Nd for the
-fused pass; FLOPs 4N^2 d + 3N^2) at this GPU's peaks, and prints one JSON
-line with a row per N.
+fused pass; FLOPs 4N^2 d + 3N^2) at this GPU's peaks; then the causal GQA
+prefill of the headline (Hq = 32, Hkv = 8, d = 128) over the same lengths,
+and the paged decode (Hq = 32, Hkv = 8, d = 128, page 16) from one long
+request to many short ones; one JSON line with a row per point.
 """
 from __future__ import annotations
 
@@ -420,15 +422,85 @@ def sweep(steps, warmup):
               file=sys.stderr, flush=True)
         del q, k, v, of, on, lf, ln
         torch.cuda.empty_cache()
+
+    def median_ms(call):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+    # the headline's causal GQA prefill over sequence length
+    causal_rows = []
+    for n in (1024, 2048, 4096, 8192, 16384, 32768):
+        inp = W.prefill_inputs(1, 32, 8, n, n, d, dtype="bf16", causal=True,
+                               seed=42)
+        q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+        del inp
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        t = median_ms(lambda: fa.fa_fwd(q, k, v, o, lse, 1, 32, 8, n, n, d,
+                                         d ** -0.5, True, fa.FA_DTYPE_BF16,
+                                         None, stream))
+        flops = 4.0 * d * 32 * n * (n + 1) / 2
+        causal_rows.append({"N": n, "ms": t,
+                            "tflops": flops / (t * 1e-3) / 1e12,
+                            "frac_bf16_peak": flops / (t * 1e-3) / 1e12 /
+                            PEAK_BF16_TFLOPS})
+        print(f"bench sweep: causal GQA N={n} {t:.3f} ms "
+              f"{flops / (t * 1e-3) / 1e12:.0f} TFLOP/s", file=sys.stderr,
+              flush=True)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+
+    # the paged decode: one long request to many short ones
+    decode_rows = []
+    for nreq, length in ((1, 32768), (1, 131072), (8, 16384), (64, 4096),
+                         (256, 1024), (512, 512)):
+        di = W.decode_inputs(nreq, 32, 8, d, lens=[length] * nreq, seed=42)
+        q = di.q.to(dev)
+        kp, vp = di.k_pool.to(dev), di.v_pool.to(dev)
+        bt, sl = di.block_table.to(dev), di.seq_lens.to(dev)
+        npages, page, hkv, _ = kp.shape
+        maxp = bt.shape[1]
+        ws = torch.empty(fa.fa_paged_decode_workspace_size(
+            nreq, 32, hkv, d, maxp, page, 0), dtype=torch.uint8, device=dev)
+        od = torch.empty((nreq, 32, d), dtype=torch.bfloat16, device=dev)
+        ld = torch.empty((nreq, 32), dtype=torch.float32, device=dev)
+        t = median_ms(lambda: fa.fa_paged_decode(
+            q, kp, vp, bt, sl, page, npages, nreq, 32, hkv, d, maxp, di.scale,
+            od, ld, ws, ws.numel(), 0, stream))
+        nbytes = decode_bytes(di, hkv, d)
+        decode_rows.append({"requests": nreq, "tokens_each": length,
+                            "ms": t, "bytes": nbytes,
+                            "GB/s": nbytes / (t * 1e-3) / 1e9,
+                            "frac_hbm_peak": nbytes / (t * 1e-3) / 1e9 /
+                            PEAK_HBM_GBS})
+        print(f"bench sweep: decode {nreq} x {length} {t:.4f} ms "
+              f"{nbytes / (t * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr,
+              flush=True)
+        del di, q, kp, vp, bt, sl, ws, od, ld
+        torch.cuda.empty_cache()
     print(json.dumps({
         "metric": "fused vs three-kernel attention forward over sequence "
                   "length (capstone roofline lab sweep)",
         "unit": "ms", "higher_is_better": False, "n_gpus": 1,
         "steps": steps, "warmup": warmup, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "B=1 H=32 d=128 non-causal N=1K..32K",
+        "config": {"workload": "B=1 H=32 d=128 non-causal N=1K..32K; causal "
+                               "GQA Hq=32 Hkv=8 d=128 N=1K..32K; paged "
+                               "decode Hq=32 Hkv=8 d=128 page 16, 1x32K .. "
+                               "512x512 tokens",
                    "seed": 42},
-        "sweep": rows}))
+        "sweep": rows, "causal_gqa": causal_rows, "decode": decode_rows}))
 
 
 def main():

@@ -437,6 +437,26 @@ def test_decode_full_workload(fa):
     _compare(o, lse, ro, rl, "bf16", name)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("lens", [[20000], [0, 30011], [100], [3000, 0, 1]])
+def test_decode_few_long_requests(fa, d, lens):
+    # few requests cut into many pieces each take the eight-wave merge: piece
+    # counts above and below one batch of 8 x 32, a request that is empty, a
+    # list shorter than the range count (empty ranges), 16 pieces a request
+    # (the one-wave merge) and 17 (the eight-wave one)
+    maxp = (max(lens) + 15) // 16 + 1
+    di = W.decode_inputs(len(lens), 32, 8, d, lens=lens, max_pages=maxp,
+                         seed=d + len(lens))
+    ro, rl = _oracle_decode(di)
+    for ns in (0, 16 * len(lens), 16 * len(lens) + 1, 300, 1000):
+        print(f"decode lens={lens} d={d} splits={ns}", flush=True)
+        o, lse = _gpu_decode(fa, di, ns)
+        _compare(o, lse, ro, rl, "bf16", f"decode {lens} d{d} splits={ns}")
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
+
+
 # ------------------------------------------------------ decode, e4m3 cache
 # The codes are widened exactly and the query stays bf16, so the bars are
 # the bf16 decode's, against the oracle on the dequantised cache.
@@ -451,6 +471,15 @@ def test_decode_fp8_cache_sweep(fa, d, hq, hkv, num_splits):
     ro, rl = _oracle_decode_fp8(di)
     _compare(o, lse, ro, rl, "bf16",
              f"fp8-cache decode d{d} {hq}/{hkv} splits={num_splits}")
+
+
+def test_decode_fp8_cache_one_long_request(fa):
+    di = W.decode_inputs(1, 32, 8, 128, lens=[25000], max_pages=1600, seed=5,
+                         kv_dtype="fp8")
+    ro, rl = _oracle_decode_fp8(di)
+    for ns in (0, 17, 777):
+        o, lse = _gpu_decode_fp8(fa, di, ns)
+        _compare(o, lse, ro, rl, "bf16", f"fp8-cache decode 1 x 25000 splits={ns}")
 
 
 def test_decode_fp8_cache_full_workload(fa):
