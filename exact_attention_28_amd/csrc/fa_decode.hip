@@ -24,10 +24,10 @@
 // page (all heads of 16 tokens, contiguous in the pool) as one block.
 //
 // The cache may also be stored as OCP e4m3 codes with per-tensor scales
-// (s_k, s_v), which halves the bytes to stream: the codes are widened
-// exactly to bf16 (K, for the MFMA) or fp32 (V, for the VALU product) in
-// registers, s_k is folded into the exp2 multiplier and s_v into the final
-// 1/l, so the arithmetic is that of the bf16 cache on the dequantised
+// (s_k, s_v), which halves the bytes to stream: the codes of K and V are
+// widened exactly to bf16 in registers for the two products, s_k is folded
+// into the exp2 multiplier and s_v into the final 1/l, so the arithmetic
+// is that of the bf16 cache on the dequantised
 // values ([FA3-guide] fp8 listing for the per-tensor scales, [FA3-paged
 // §3.2] for the pages).
 //
@@ -39,9 +39,13 @@
 //     (lane: head l%16; heads past the group are zero);
 //   * online softmax per head (column): lane-local over 4 tokens, then two
 //     cross-row steps, with the lazy rescale of the prefill kernels;
-//   * O[head, d] += P V on the VALU: a lane owns 4 tokens and D/16 d
-//     columns, P is broadcast inside each 16-lane row with DPP
-//     row_newbcast, V is read 16 B per lane from HBM.
+//   * O[head, d] += P V on v_mfma_f32_16x16x16_bf16, P rounded to bf16
+//     (the A operand is the score step's output layout, so P never moves
+//     between lanes); a lane reads the V rows of its 4 tokens, D/16
+//     contiguous d each, straight from HBM, and byte permutes pair the rows
+//     into the B operand (an e4m3 pair is then widened exactly to bf16).
+//     O is divided by the sum of the rounded P, the log-sum-exp takes the
+//     sum of the unrounded P.
 #include <mutex>
 #include <type_traits>
 
@@ -96,17 +100,6 @@ struct PageRegs<D, true> {
   typedef uint32_t vrow_t __attribute__((ext_vector_type(D / 64)));
   vrow_t v[4];
 };
-// e4m3 codes -> fp32 values (exact), two per conversion
-__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* out) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  out[0] = lo[0];
-  out[1] = lo[1];
-  out[2] = hi[0];
-  out[3] = hi[1];
-}
-
 __device__ __forceinline__ int pages_of(int len, int max_len) {
   len = max(0, min(len, max_len));
   return (len + kPage - 1) / kPage;
@@ -134,32 +127,43 @@ __device__ __forceinline__ float lane_value(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-// Lane n of every 16-lane row, broadcast to the whole row (DPP
-// row_newbcast): P of head n for the four tokens this row holds.
-template <int N>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(
-      0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+// O[head, d] += P[head, token] V[token, d] over one page's 16 tokens on
+// v_mfma_f32_16x16x16_bf16: A = P (lane: head l%16, tokens 4*(l/16)+0..3,
+// as the score step leaves them), B = V (lane: column l%16, the same four
+// tokens). Product j takes d = DL*(l%16) + j for column l%16, so a lane's
+// V rows, DL contiguous d each, feed the products without crossing lanes,
+// and the result of product j for head 4*(l/16)+v at d = DL*(l%16)+j sits
+// in element v of accumulator j of lane l.
+__device__ __forceinline__ f32x4 mfma_16x16x16_bf16(uint32_t a01, uint32_t a23,
+                                                    uint32_t b01, uint32_t b23,
+                                                    f32x4 c) {
+  const i16x4 a = __builtin_bit_cast(i16x4, u32x2{a01, a23});
+  const i16x4 b = __builtin_bit_cast(i16x4, u32x2{b01, b23});
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-// o[g][:] += P[token, g] * v[:] for g < G (compile-time unrolled so the
-// DPP lane selector is a constant).
-template <int G, int GP, int DL>
-struct PvAccumulate {
-  static __device__ __forceinline__ void run(float (&o)[GP][DL], float p,
-                                             const float (&vf)[DL]) {
-    PvAccumulate<G - 1, GP, DL>::run(o, p, vf);
-    const float pg = row_bcast<G - 1>(p);
-#pragma unroll
-    for (int e = 0; e < DL; ++e) o[G - 1][e] = __builtin_fmaf(pg, vf[e], o[G - 1][e]);
-  }
-};
-template <int GP, int DL>
-struct PvAccumulate<0, GP, DL> {
-  static __device__ __forceinline__ void run(float (&)[GP][DL], float,
-                                             const float (&)[DL]) {}
-};
+// bf16 pairs: the low (or high) halves of two rows' words, row x first
+__device__ __forceinline__ uint32_t lo_halves(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+// e4m3 codes of two rows interleaved: bytes (x0, y0, x1, y1) (or of
+// bytes 2 and 3), each pair then widened exactly to a bf16 pair
+__device__ __forceinline__ uint32_t codes_lo(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05010400u);
+}
+__device__ __forceinline__ uint32_t codes_hi(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07030602u);
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair_bf16(uint32_t w) {
+  return __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.f, HI));
+}
 
-template <int D, int GP, int NW, bool KV8>
+template <int D, int NW, bool KV8>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
     KParams a, const __bf16* __restrict__ Qp, const void* __restrict__ KPv,
     const void* __restrict__ VPv, const int32_t* __restrict__ BT,
@@ -252,8 +256,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   // query heads of the group as the B operand: head col, d = 32s + 8*row16
   // (e4m3 cache: d = (D/4)*row16 + 8s, the K codes' order)
   bf16x8 qf[D / 32];
-  float m, lp;  // exponent reference of head `col`; its partial sum
-  float o[GP][DL];
+  // exponent reference of head `col`; its partial sums of P, unrounded (for
+  // the log-sum-exp) and as rounded to bf16 for the products (for O)
+  float m, lp, lr;
+  f32x4 oacc[DL];
   bool piece_bad;
 
   auto process = [&](const Regs& pr_in, bool bad, int page, int lim) {
@@ -292,12 +298,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
       const float mnew = fmaxf(m, mxs);
       const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - mnew);
       lp *= alpha;
+      lr *= alpha;
       m = mnew;
+      // heads 4*row16 + v of this lane's accumulators: alpha of lane col = head
 #pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        const float ag = lane_value(alpha, g);
+      for (int v = 0; v < 4; ++v) {
+        const float av = __shfl(alpha, 4 * row16 + v, 64);
 #pragma unroll
-        for (int e = 0; e < DL; ++e) o[g][e] *= ag;
+        for (int j = 0; j < DL; ++j) oacc[j][v] *= av;
       }
     }
     const float mref = (m == kNegInf) ? 0.f : m;
@@ -307,28 +315,45 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
       pr[v] = fast_exp2(__builtin_fmaf(acc[v], a.c, -mref));
       lp += pr[v];
     }
-    // O[g, d] += sum over this lane's 4 tokens of P[token, g] * V[token, d].
-    // A token past the piece (the tail of a request's last page) has P = 0,
-    // but its V row is a cache slot whose contents are unspecified: it is
-    // taken as 0, so that 0 * NaN cannot reach O.
+    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
+    const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
+    lr = add_bf16x2(p23, add_bf16x2(p01, lr));
+    // V rows of the lane's four tokens. A token past the piece (the tail of
+    // a request's last page) has P = 0, but its V row is a cache slot whose
+    // contents are unspecified: it is taken as 0, so that 0 * NaN cannot
+    // reach O.
+    typename Regs::vrow_t vr[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      float vf[DL];
-      if constexpr (!KV8) {
+      vr[rr] = pr_in.v[rr];
+      if (tok0 + rr >= lim) vr[rr] = typename Regs::vrow_t{};
+    }
+    if constexpr (!KV8) {
+      // word e of a row holds d = DL*col + 2e (low half) and 2e + 1
 #pragma unroll
-        for (int e = 0; e < DL / 2; ++e) {
-          vf[2 * e] = bf16_lo(pr_in.v[rr][e]);
-          vf[2 * e + 1] = bf16_hi(pr_in.v[rr][e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < DL / 4; ++e) e4m3x4_to_f32(pr_in.v[rr][e], vf + 4 * e);
+      for (int e = 0; e < DL / 2; ++e) {
+        oacc[2 * e] = mfma_16x16x16_bf16(p01, p23, lo_halves(vr[0][e], vr[1][e]),
+                                         lo_halves(vr[2][e], vr[3][e]), oacc[2 * e]);
+        oacc[2 * e + 1] = mfma_16x16x16_bf16(p01, p23, hi_halves(vr[0][e], vr[1][e]),
+                                             hi_halves(vr[2][e], vr[3][e]), oacc[2 * e + 1]);
       }
-      if (tok0 + rr >= lim) {
+    } else {
+      // word e of a row holds the codes of d = DL*col + 4e + (0..3)
 #pragma unroll
-        for (int e = 0; e < DL; ++e) vf[e] = 0.f;
+      for (int e = 0; e < DL / 4; ++e) {
+        const uint32_t x01 = codes_lo(vr[0][e], vr[1][e]);
+        const uint32_t x23 = codes_lo(vr[2][e], vr[3][e]);
+        const uint32_t y01 = codes_hi(vr[0][e], vr[1][e]);
+        const uint32_t y23 = codes_hi(vr[2][e], vr[3][e]);
+        oacc[4 * e] = mfma_16x16x16_bf16(p01, p23, e4m3_pair_bf16<false>(x01),
+                                         e4m3_pair_bf16<false>(x23), oacc[4 * e]);
+        oacc[4 * e + 1] = mfma_16x16x16_bf16(p01, p23, e4m3_pair_bf16<true>(x01),
+                                             e4m3_pair_bf16<true>(x23), oacc[4 * e + 1]);
+        oacc[4 * e + 2] = mfma_16x16x16_bf16(p01, p23, e4m3_pair_bf16<false>(y01),
+                                             e4m3_pair_bf16<false>(y23), oacc[4 * e + 2]);
+        oacc[4 * e + 3] = mfma_16x16x16_bf16(p01, p23, e4m3_pair_bf16<true>(y01),
+                                             e4m3_pair_bf16<true>(y23), oacc[4 * e + 3]);
       }
-      PvAccumulate<GP, GP, DL>::run(o, pr[rr], vf);
     }
   };
 
@@ -360,10 +385,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     }
     m = kNegInf;
     lp = 0.f;
+    lr = 0.f;
 #pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-      for (int e = 0; e < DL; ++e) o[g][e] = 0.f;
+    for (int j = 0; j < DL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     piece_bad = false;
 
     // NS page slots, each reloaded right after it is computed. Loads past
@@ -395,49 +419,43 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     // partial in slot b + r.
     const bool first = p == 0, req_end = pe == n;
     const bool whole = first && req_end;
-#pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-      for (int e = 0; e < DL; ++e) {
-        float t = o[g][e];
-        t += xor_lane(t, 16);
-        t += xor_lane(t, 32);
-        o[g][e] = t;
-      }
+    // per head (lane col): sums over the four token rows, the scale of O and
+    // the log-sum-exp; then to the lanes that hold the head's outputs
     float ls = lp + xor_lane(lp, 16);
     ls += xor_lane(ls, 32);
+    float lrs = lr + xor_lane(lr, 16);
+    lrs += xor_lane(lrs, 32);
+    const bool live = ls > 0.f;
+    float inv = live ? a.sv / lrs : 0.f;
+    float lse = live ? (m + fast_log2(ls)) * kLn2 : kNegInf;
+    if (piece_bad) {
+      inv = __builtin_nanf("");
+      lse = __builtin_nanf("");
+    }
 #pragma unroll
-    for (int g = 0; g < GP; ++g) {
+    for (int v = 0; v < 4; ++v) {
+      const int g = 4 * row16 + v;
+      const float inv_g = __shfl(inv, g, 64);
+      const float lse_g = __shfl(lse, g, 64);
       if (g >= G) continue;
-      const float mg = lane_value(m, g);
-      const float lg = lane_value(ls, g);
-      const bool live = lg > 0.f;
-      float inv = live ? a.sv / lg : 0.f;
-      float lse = live ? (mg + fast_log2(lg)) * kLn2 : kNegInf;
-      if (piece_bad) {
-        inv = __builtin_nanf("");
-        lse = __builtin_nanf("");
-      }
-      if (row16 == (g & 3)) {
-        const long hq = (long)b * a.Hq + (long)hkv * G + g;
-        if (whole) {
-          vload_t st;
+      const long hq = (long)b * a.Hq + (long)hkv * G + g;
+      if (whole) {
+        vload_t st;
 #pragma unroll
-          for (int e = 0; e < DL / 2; ++e)
-            st[e] = pack_bf16x2(o[g][2 * e] * inv, o[g][2 * e + 1] * inv);
-          *reinterpret_cast<vload_t*>(O + hq * D + DL * col) = st;
-          if (col == 0 && LSE != nullptr) LSE[hq] = lse;
-        } else {
-          const long ph = ((long)b + r) * a.Hq + (long)hkv * G + g;
-          float* po = ws_o + ph * D + DL * col;
+        for (int e = 0; e < DL / 2; ++e)
+          st[e] = pack_bf16x2(oacc[2 * e][v] * inv_g, oacc[2 * e + 1][v] * inv_g);
+        *reinterpret_cast<vload_t*>(O + hq * D + DL * col) = st;
+        if (col == 0 && LSE != nullptr) LSE[hq] = lse_g;
+      } else {
+        const long ph = ((long)b + r) * a.Hq + (long)hkv * G + g;
+        float* po = ws_o + ph * D + DL * col;
 #pragma unroll
-          for (int e = 0; e < DL; e += 4) {
-            f32x4 t = {o[g][e] * inv, o[g][e + 1] * inv, o[g][e + 2] * inv,
-                       o[g][e + 3] * inv};
-            *reinterpret_cast<f32x4*>(po + e) = t;
-          }
-          if (col == 0) ws_l[ph] = lse;
+        for (int e = 0; e < DL; e += 4) {
+          f32x4 t = {oacc[e][v] * inv_g, oacc[e + 1][v] * inv_g,
+                     oacc[e + 2][v] * inv_g, oacc[e + 3][v] * inv_g};
+          *reinterpret_cast<f32x4*>(po + e) = t;
         }
+        if (col == 0) ws_l[ph] = lse_g;
       }
     }
     if (hkv == 0 && lane == 0) {
@@ -656,33 +674,21 @@ __global__ __launch_bounds__(512) void decode_merge_wide_kernel(
   if (lane == 0 && LSE != nullptr) LSE[hq] = L_out;
 }
 
-template <int D, int GP, int NW, bool KV8>
+template <int D, int NW, bool KV8>
 void* kernel_ptr() {
-  return reinterpret_cast<void*>(&decode_kernel<D, GP, NW, KV8>);
+  return reinterpret_cast<void*>(&decode_kernel<D, NW, KV8>);
 }
 
-// Kernel instance for head dim d, group size G, waves per workgroup nw and
-// the cache's storage (bf16 or e4m3 codes).
+// Kernel instance for head dim d, waves per workgroup nw and the cache's
+// storage (bf16 or e4m3 codes); every group size up to 16 heads shares it
+// (the heads are the rows of the products).
 template <bool KV8>
-void* select_kernel_t(int d, int G, int nw) {
-#define FA_PICK8(DD, NWW)                                         \
-  if (G <= 1) return kernel_ptr<DD, 1, NWW, KV8>();               \
-  if (G <= 2) return kernel_ptr<DD, 2, NWW, KV8>();               \
-  if (G <= 4) return kernel_ptr<DD, 4, NWW, KV8>();               \
-  return kernel_ptr<DD, 8, NWW, KV8>();
-  // eight-wave workgroups are planned only for groups of <= 8 heads
-  if (d == 128) {
-    if (nw == 8) { FA_PICK8(128, 8) }
-    if (G > 8) return kernel_ptr<128, 16, 4, KV8>();
-    FA_PICK8(128, 4)
-  }
-  if (nw == 8) { FA_PICK8(64, 8) }
-  if (G > 8) return kernel_ptr<64, 16, 4, KV8>();
-  FA_PICK8(64, 4)
-#undef FA_PICK8
+void* select_kernel_t(int d, int nw) {
+  if (d == 128) return nw == 8 ? kernel_ptr<128, 8, KV8>() : kernel_ptr<128, 4, KV8>();
+  return nw == 8 ? kernel_ptr<64, 8, KV8>() : kernel_ptr<64, 4, KV8>();
 }
-void* select_kernel(int d, int G, int nw, bool kv8) {
-  return kv8 ? select_kernel_t<true>(d, G, nw) : select_kernel_t<false>(d, G, nw);
+void* select_kernel(int d, int nw, bool kv8) {
+  return kv8 ? select_kernel_t<true>(d, nw) : select_kernel_t<false>(d, nw);
 }
 
 // Waves the current device holds at once for this kernel instance.
@@ -725,7 +731,7 @@ hipError_t decode_scratch(void** ptr) {
 bool plan_decode(int B, int Hq, int Hkv, int d, int max_pages, int num_splits,
                  DecodePlan* p) {
   const int G = Hq / Hkv;
-  const int nw = (Hkv % 8 == 0 && G <= 8) ? 8 : 4;
+  const int nw = Hkv % 8 == 0 ? 8 : 4;
   // heads per workgroup: the divisor of Hkv <= nw that keeps most waves busy
   int hh = 1;
   for (int c = 1; c <= nw; ++c)
@@ -740,7 +746,7 @@ bool plan_decode(int B, int Hq, int Hkv, int d, int max_pages, int num_splits,
   } else {
     // sized by the bf16 instance for both storages, so one workspace query
     // serves both entry points
-    const int waves = resident_waves(select_kernel(d, G, nw, false), nw);
+    const int waves = resident_waves(select_kernel(d, nw, false), nw);
     R = waves / Hkv;
   }
   R = ((R + p->waves_per_head - 1) / p->waves_per_head) * p->waves_per_head;
@@ -778,7 +784,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p) {
   float* ws_l = static_cast<float*>(a.ws) + p.off_l;
   __bf16* o = static_cast<__bf16*>(a.o);
   float* lse = a.lse;
-  void* fn = select_kernel(a.d, k.G, p.nw, a.kv_fp8);
+  void* fn = select_kernel(a.d, p.nw, a.kv_fp8);
   void* args[] = {&k, &q, &kp, &vp, &bt, &sl, &wsi, &ws_o, &ws_l, &o, &lse};
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.grid),
                                  dim3((unsigned)(p.nw * 64)), args, 0,

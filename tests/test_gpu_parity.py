@@ -354,7 +354,8 @@ def _oracle_decode(di):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (32, 8), (16, 1), (6, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (32, 8), (16, 1), (6, 2),
+                                    (128, 8)])
 @pytest.mark.parametrize("num_splits", [0, 1, 3])
 def test_decode_sweep(fa, d, hq, hkv, num_splits):
     lens = [0, 1, 15, 16, 17, 31, 33, 100, 255, 256, 257, 1000]
@@ -461,7 +462,7 @@ def test_decode_few_long_requests(fa, d, lens):
 # The codes are widened exactly and the query stays bf16, so the bars are
 # the bf16 decode's, against the oracle on the dequantised cache.
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (16, 1), (6, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (16, 1), (6, 2), (128, 8)])
 @pytest.mark.parametrize("num_splits", [0, 1, 3])
 def test_decode_fp8_cache_sweep(fa, d, hq, hkv, num_splits):
     lens = [0, 1, 15, 16, 17, 31, 33, 100, 255, 256, 257, 1000]
