@@ -753,11 +753,12 @@ def main():
         out["value"] = tf
         out["unit"] = "TFLOPS"
         out["roofline"] = {
-            "kernel": "fwd_bf16_kernel<128, causal>",
+            "kernel": "fwd_bf16_pp_kernel<causal>",
             "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
             "traffic": _traffic("fwd_bf16_causal_n16384",
-                                ["fa_fwd_bf16.hip", "fa_device.h"]),
+                                ["fa_fwd_bf16_pp.hip", "fa_pp_asm.h",
+                                 "fa_device.h"]),
             "algorithmic_gflop_per_launch": info["prefill"]["flops"] / 1e9,
             # the pages' 3 softmax FLOPs per score, kept out of TFLOPS
             "softmax_gflop_per_launch": 0.75 * info["prefill"]["flops"]

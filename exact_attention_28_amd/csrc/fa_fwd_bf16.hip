@@ -508,8 +508,7 @@ hipError_t launch(const FwdArgs& a, const PagedKV& pk) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
   const PagedKV none{nullptr, nullptr, 0, 0};
-  if (a.d == 128)
-    return a.causal ? launch<128, true, false>(a, none) : launch<128, false, false>(a, none);
+  if (a.d == 128) return launch_fwd_bf16_pp(a);
   return a.causal ? launch<64, true, false>(a, none) : launch<64, false, false>(a, none);
 }
 

@@ -63,6 +63,9 @@ hipError_t launch_paged_prefill_bf16(const FwdArgs& a, const int32_t* bt,
                                      const int32_t* sl, int max_pages,
                                      int num_pages);
 hipError_t launch_fwd_fp8(const FwdArgs& a);
+// The bf16 forward at d = 128 over contiguous K/V with the two waves of each
+// SIMD in opposite phases (matrix phase written out as inline asm).
+hipError_t launch_fwd_bf16_pp(const FwdArgs& a);
 
 struct DecodeArgs {
   const void* q;
