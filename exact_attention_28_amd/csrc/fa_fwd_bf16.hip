@@ -515,9 +515,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a) {
 hipError_t launch_paged_prefill_bf16(const FwdArgs& a, const int32_t* bt,
                                      const int32_t* sl, int max_pages,
                                      int num_pages) {
+  if (a.d == 128) return launch_paged_prefill_bf16_pp(a, bt, sl, max_pages, num_pages);
   const PagedKV pk{bt, sl, max_pages, num_pages};
-  if (a.d == 128)
-    return a.causal ? launch<128, true, true>(a, pk) : launch<128, false, true>(a, pk);
   return a.causal ? launch<64, true, true>(a, pk) : launch<64, false, true>(a, pk);
 }
 

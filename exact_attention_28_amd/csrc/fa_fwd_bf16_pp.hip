@@ -1,5 +1,6 @@
-// fa_fwd_bf16_pp.hip - exact attention forward, bf16, d = 128, contiguous
-// K/V, gfx950: the two waves of each SIMD in opposite phases.
+// fa_fwd_bf16_pp.hip - exact attention forward, bf16, d = 128, gfx950: the
+// two waves of each SIMD in opposite phases. K/V contiguous, or a paged
+// cache (the chunked prefill of [FA3-paged §3.2]).
 //
 // The method is the bf16 forward's ([Capstone §4.1] Q-outer / KV-inner
 // order, online softmax of §2.2 with the deferred 1/l of §4.2, causal tiles
@@ -51,6 +52,19 @@ constexpr int kLPW = kNB / 4;   // blocks each loading wave moves per tile
 constexpr int kTileBytes = kNB * kPitch;
 constexpr int kKBufs = 2, kVBufs = 3;
 
+// Where K and V come from when PAGED: the cache of request b is
+// seq_lens[b] tokens in 16-token pages of a [num_pages, 16, Hkv, d] pool,
+// logical page p at physical page block_table[b, p]; the Nq queries are the
+// request's last Nq positions (bottom-right causal alignment).
+struct PagedCache {
+  const int32_t* bt;  // [B, max_pages]
+  const int32_t* sl;  // [B]
+  int max_pages, num_pages;
+};
+constexpr int kMaxPagesLds = 8192;  // page-table entries a workgroup stages
+constexpr int kMaxRankB = 256;      // batches up to this size run longest first
+static_assert(kMaxRankB <= kThreads, "one request length per thread");
+
 // LDS layout of a tile (as in the other bf16 forward): K block b holds
 // rows b, b + 16, b + 32, b + 48 (conflict-free 16-byte row reads of 16
 // consecutive keys); V block (r % 4) * 4 + r / 16 holds row r at slot
@@ -76,12 +90,12 @@ __device__ __forceinline__ void g2lds_16B_sbase(const void* base, uint32_t off,
                : "memory");
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pp_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,
-    float c) {
+    float c, PagedCache pk) {
   __shared__ __attribute__((aligned(16))) char lds[(kKBufs + kVBufs) * kTileBytes];
   __shared__ int redo;
   const uint32_t lds0 = (uint32_t)(size_t)(lds_char*)lds;
@@ -98,11 +112,62 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pp_kernel(
   const TileIdx ti = map_tile(blockIdx.x, n_qt, Hq, Hkv, B, CAUSAL);
   const int hk = ti.hq / (Hq / Hkv);
   const int q0 = ti.qt * kBM;
-  const long qbase = (long)(ti.b * Hq + ti.hq) * Nq * kD;
-  const long kv_head = (long)(ti.b * Hkv + hk) * Nk * kD;
+  // The batch index this workgroup serves. For the paged cache, whose
+  // requests differ in length, the logical index is a rank: requests are
+  // taken longest first (ties by index), so the longest workgroups start
+  // first and the grid ends without a ragged tail. Each workgroup ranks the
+  // lengths itself (a batch of at most kMaxRankB requests; larger batches
+  // keep their order).
+  int bq = ti.b;
+  if constexpr (PAGED) {
+    if (B <= kMaxRankB) {
+      __shared__ int lens[kMaxRankB];
+      __shared__ int ranked;
+      const int cap = pk.max_pages * 16;
+      if (tid < B) lens[tid] = max(0, min(pk.sl[tid], cap));
+      __syncthreads();
+      if (tid < B) {
+        const int lr = lens[tid];
+        int rank = 0;
+        for (int r2 = 0; r2 < B; ++r2) {
+          const int l2 = lens[r2];
+          rank += (l2 > lr) || (l2 == lr && r2 < tid);
+        }
+        if (rank == ti.b) ranked = tid;
+      }
+      __syncthreads();
+      bq = ranked;
+    }
+  }
+  const long qbase = (long)(bq * Hq + ti.hq) * Nq * kD;
+  // keys of this request; for the paged cache its length, and the page
+  // table staged in LDS (ids outside the pool are replaced by 0 and turn
+  // the request's output to NaN)
+  __shared__ int page_ids[PAGED ? kMaxPagesLds : 1];
+  __shared__ int page_bad;
+  int nk = Nk;
+  if constexpr (PAGED) {
+    nk = max(0, min(pk.sl[bq], pk.max_pages * 16));
+    const int np = (nk + 15) / 16;
+    if (tid == 0) page_bad = 0;
+    __syncthreads();
+    bool bad = false;
+    for (int i = tid; i < np; i += kThreads) {
+      const int id = pk.bt[(long)bq * pk.max_pages + i];
+      const bool ok = id >= 0 && id < pk.num_pages;
+      page_ids[i] = ok ? id : 0;
+      bad |= !ok;
+    }
+    if (bad) page_bad = 1;
+    __syncthreads();
+  }
+  // contiguous: the head's K/V; paged: the pool plus this head's offset
+  // within a token row (rows of a page are Hkv * d apart)
+  const long kv_head = PAGED ? (long)hk * kD : (long)(bq * Hkv + hk) * Nk * kD;
   const __bf16* Kh = K + kv_head;
   const __bf16* Vh = V + kv_head;
-  const int nk = Nk;
+  const long tok_stride = PAGED ? (long)Hkv * kD : kD;
+  const uint32_t page_elems = 16u * (uint32_t)tok_stride;
   const int off = nk - Nq;  // bottom-right causal alignment
   int kend = nk;
   if (CAUSAL) kend = min(nk, min(q0 + kBM, Nq) + off);
@@ -130,29 +195,44 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pp_kernel(
   // scores are masked, their P is 0).
   const int fw = w & 3;
   const int slot = lane >> 4, chunk = lane & 15;
-  int krow[kLPW], vrow[kLPW];
-  uint32_t kofs[kLPW], vofs[kLPW];
-#pragma unroll
-  for (int i = 0; i < kLPW; ++i) {
-    krow[i] = k_row(fw + 4 * i, slot);
-    vrow[i] = v_row(fw + 4 * i, slot);
-    kofs[i] = (uint32_t)(krow[i] * kD + 8 * chunk) * 2u;
-    vofs[i] = (uint32_t)(vrow[i] * kD + 8 * chunk) * 2u;
-  }
-  auto issue = [&](const __bf16* src, const int (&rows)[kLPW],
-                   const uint32_t (&ofs)[kLPW], int tile, uint32_t buf)
-      __attribute__((always_inline)) {
+  // The four rows a lane moves are tile rows k_row(fw + 4i, slot) =
+  // fw + 16 slot + 4i of K and v_row(fw + 4i, slot) = 16 fw + 4 slot + i of
+  // V: one per-lane row plus a step of 4 (K) or 1 (V) rows per load. In a
+  // paged cache a full tile is four whole pages, and these rows lie in one
+  // of them (K: page `slot` of the tile, V: page `fw`).
+  const int krow0 = k_row(fw, slot), vrow0 = v_row(fw, slot);
+  constexpr int kStepK = 4, kStepV = 1;  // rows between a lane's loads
+  auto issue = [&](const __bf16* src, int row0, int step, int page, int tile,
+                   uint32_t buf) __attribute__((always_inline)) {
     const int n0 = tile * kBN;
-    if (n0 + kBN <= nk) {
+    if (!PAGED && n0 + kBN <= nk) {
       const __bf16* base = src + (long)n0 * kD;
+      const uint32_t ofs = (uint32_t)(row0 * kD + 8 * chunk) * 2u;
 #pragma unroll
       for (int i = 0; i < kLPW; ++i)
-        g2lds_16B_sbase(base, ofs[i], (lds_char*)(size_t)(buf + (fw + 4 * i) * kPitch));
+        g2lds_16B_sbase(base + (long)i * step * kD, ofs,
+                        (lds_char*)(size_t)(buf + (fw + 4 * i) * kPitch));
+    } else if (PAGED && n0 + kBN <= nk) {
+      const __bf16* base =
+          src + (long)((uint64_t)(uint32_t)page_ids[(n0 >> 4) + page] * page_elems) +
+          (long)(row0 & 15) * tok_stride + 8 * chunk;
+#pragma unroll
+      for (int i = 0; i < kLPW; ++i)
+        g2lds_16B_own(base + (long)i * step * tok_stride,
+                      (lds_char*)(size_t)(buf + (fw + 4 * i) * kPitch));
     } else {
+      // the ragged last tile: rows past the keys clamped to the last key
+      // (their scores are masked, their P is 0); paged: token t of the
+      // request sits at row t % 16 of page page_ids[t / 16]
 #pragma unroll
       for (int i = 0; i < kLPW; ++i) {
-        const int r = n0 + min(rows[i], nk - 1 - n0);
-        g2lds_16B_own(src + (long)r * kD + 8 * chunk,
+        const int t = n0 + min(row0 + i * step, nk - 1 - n0);
+        long e;
+        if constexpr (PAGED)
+          e = ((long)page_ids[t >> 4] * 16 + (t & 15)) * tok_stride;
+        else
+          e = (long)t * kD;
+        g2lds_16B_own(src + e + 8 * chunk,
                       (lds_char*)(size_t)(buf + (fw + 4 * i) * kPitch));
       }
     }
@@ -160,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pp_kernel(
   auto issue_all = [&](int tile, auto which) __attribute__((always_inline)) {
     // which: 0 both (the prologue), 1 K, 2 V
     constexpr int WH = decltype(which)::value;
-    if (WH != 2) issue(Kh, krow, kofs, tile, kbuf(tile));
-    if (WH != 1) issue(Vh, vrow, vofs, tile, vbuf(tile));
+    if (WH != 2) issue(Kh, krow0, kStepK, slot, tile, kbuf(tile));
+    if (WH != 1) issue(Vh, vrow0, kStepV, fw, tile, vbuf(tile));
   };
 
   // per-lane fragment bases within a tile
@@ -320,7 +400,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pp_kernel(
   const float lrtot = sum_halves(st.lr);
   if (row < Nq) {
     const bool live = ltot > 0.f;
-    const float inv = live ? 1.f / lrtot : 0.f;
+    float inv = live ? 1.f / lrtot : 0.f;
+    bool nan_out = false;
+    if constexpr (PAGED) nan_out = page_bad != 0;
+    if (nan_out) inv = __builtin_nanf("");
     __bf16* orow = O + qbase + (long)row * kD;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -332,22 +415,36 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pp_kernel(
         *reinterpret_cast<u32x2*>(orow + 32 * mb + 8 * g + 4 * h) = pr;
       }
     if (h == 0 && LSE != nullptr)
-      LSE[(long)(ti.b * Hq + ti.hq) * Nq + row] =
-          live ? (st.m + fast_log2(ltot)) * kLn2 : kNegInf;
+      LSE[(long)(bq * Hq + ti.hq) * Nq + row] =
+          nan_out ? __builtin_nanf("")
+                  : (live ? (st.m + fast_log2(ltot)) * kLn2 : kNegInf);
   }
+}
+
+template <bool CAUSAL, bool PAGED>
+hipError_t launch(const FwdArgs& a, const PagedCache& pk) {
+  const int n_qt = (a.Nq + kBM - 1) / kBM;
+  const long blocks = (long)n_qt * a.Hq * a.B;
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<CAUSAL, PAGED>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.q),
+                     static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
+                     static_cast<__bf16*>(a.o), a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+                     a.scale * kLog2e, pk);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16_pp(const FwdArgs& a) {
-  const int n_qt = (a.Nq + kBM - 1) / kBM;
-  const long blocks = (long)n_qt * a.Hq * a.B;
-  auto kern = a.causal ? fwd_bf16_pp_kernel<true> : fwd_bf16_pp_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse,
-                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e);
-  return hipGetLastError();
+  const PagedCache none{nullptr, nullptr, 0, 0};
+  return a.causal ? launch<true, false>(a, none) : launch<false, false>(a, none);
+}
+
+hipError_t launch_paged_prefill_bf16_pp(const FwdArgs& a, const int32_t* bt,
+                                        const int32_t* sl, int max_pages,
+                                        int num_pages) {
+  const PagedCache pk{bt, sl, max_pages, num_pages};
+  return a.causal ? launch<true, true>(a, pk) : launch<false, true>(a, pk);
 }
 
 }  // namespace fa

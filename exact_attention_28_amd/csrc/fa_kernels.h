@@ -63,9 +63,13 @@ hipError_t launch_paged_prefill_bf16(const FwdArgs& a, const int32_t* bt,
                                      const int32_t* sl, int max_pages,
                                      int num_pages);
 hipError_t launch_fwd_fp8(const FwdArgs& a);
-// The bf16 forward at d = 128 over contiguous K/V with the two waves of each
-// SIMD in opposite phases (matrix phase written out as inline asm).
+// The bf16 forward at d = 128 with the two waves of each SIMD in opposite
+// phases (matrix phase written out as inline asm): contiguous K/V, and over
+// a paged cache (arguments as launch_paged_prefill_bf16).
 hipError_t launch_fwd_bf16_pp(const FwdArgs& a);
+hipError_t launch_paged_prefill_bf16_pp(const FwdArgs& a, const int32_t* bt,
+                                        const int32_t* sl, int max_pages,
+                                        int num_pages);
 
 struct DecodeArgs {
   const void* q;
