@@ -857,7 +857,7 @@ def main():
         tf = info["chunked"]["flops"] / t / 1e12
         out["chunked_prefill"] = {
             "value": tf, "unit": "TFLOPS", "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
-            "kernel": "fwd_bf16_kernel<paged>",
+            "kernel": "fwd_bf16_pp_kernel<causal, paged>",
             **_at_clock(tf, PEAK_BF16_TFLOPS, *clock["chunked"]),
             **_launch_stats(ms["chunked"])}
         workload.append("chunked prefill 16 requests x 512 new tokens, paged "
