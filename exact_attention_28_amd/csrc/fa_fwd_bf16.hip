@@ -1,4 +1,9 @@
-// fa_fwd_bf16.hip - exact attention forward, bf16 in / bf16 out, gfx950.
+// fa_fwd_bf16.hip - exact attention forward, bf16 in / bf16 out, gfx950,
+// for d = 64 (contiguous and paged K/V). At d = 128 the launchers below hand
+// the call to fwd_bf16_pp_kernel (fa_fwd_bf16_pp.hip), which computes the
+// same arithmetic in the same order with the two waves of each SIMD in
+// opposite phases; this kernel interleaves each wave's products and vector
+// work within one basic block instead.
 //
 // One workgroup (8 waves, one per CU) owns a 256-row query tile of one
 // (batch, head) and streams the key/value range in 64-key tiles: the
